@@ -1,0 +1,180 @@
+/*
+ * gqa.h -- C interface of libgqa: grouped-query attention over a KV cache on
+ * AMD Instinct MI355X (gfx950), for single-token decode and causal prefill,
+ * with an optional local window that includes the current cell.
+ *
+ * What is computed ("Share key/value heads and make context explicit",
+ * sections "Give each query head an explicit shared KV head" and "Intersect
+ * the window with the context already permitted"):
+ *
+ *   r = Hq / Hkv; query head h reads KV head g(h) = floor(h / r).
+ *   An active query at cell t of batch row b (t < n_b) may read the key cells
+ *   l..t, where l = 0 without a window and l = max(0, t - (w - 1)) with a
+ *   window of w >= 1 cells (the current cell plus at most w - 1 earlier ones).
+ *   s_j = scale * <q_{h,t}, k_{g(h),j}>, p = softmax of s over l..t only
+ *   (every other cell has probability exactly 0), z_{h,t} = sum_j p_j v_{g,j}.
+ *   The output row of cell t concatenates z_{0,t} .. z_{Hq-1,t} in head order.
+ *   Inactive (padded) queries, t >= n_b, produce a zero row.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named q, k_cache, v_cache, out, seqlens, workspace and records
+ *     are DEVICE pointers owned by the caller; the library never allocates,
+ *     frees or keeps them.  All arrays are dense and contiguous with the last
+ *     axis (d) innermost.
+ *   - dtype selects the element type of q, k_cache, v_cache and out together:
+ *     GQA_F32 (IEEE binary32) or GQA_BF16 (bfloat16).  Arithmetic is fp32
+ *     throughout; bf16 outputs are rounded to nearest even.
+ *   - window < 0 means no local window; window == 0 is refused
+ *     (GQA_ERR_ZERO_WINDOW); window >= 1 is the window length in cells.
+ *   - scale multiplies the dot products; pass 1/sqrt(d) for the usual scaled
+ *     dot product.  It must be finite.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return; they never synchronise.
+ *   - Every argument check happens on the host before anything is enqueued;
+ *     on any error nothing is launched and out is left untouched (a failed
+ *     call never half-advances anything, as the pages require of the cache).
+ *   - Preconditions that live in device memory are NOT checked (checking would
+ *     need a synchronisation): 0 <= seqlens[b] <= T for prefill and
+ *     0 <= seqlens[b] <= C for decode.
+ *   - Calls are thread-safe; the library holds no mutable state.
+ */
+#ifndef GQA_H
+#define GQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GQA_OK = 0,
+    GQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    GQA_ERR_HEADS = 2,       /* Hq <= 0, Hkv <= 0 or Hq % Hkv != 0                 */
+    GQA_ERR_ZERO_WINDOW = 3, /* window == 0                                        */
+    GQA_ERR_HEAD_DIM = 4,    /* d < 1 or d > 256                                   */
+    GQA_ERR_DTYPE = 5,       /* dtype is not GQA_F32 or GQA_BF16                   */
+    GQA_ERR_SHAPE = 6,       /* negative B/T/C, T > C, or a grid limit exceeded    */
+    GQA_ERR_OVERFLOW = 7,    /* an element count or byte size overflows int64      */
+    GQA_ERR_WORKSPACE = 8,   /* workspace smaller than gqa_decode_workspace_bytes  */
+    GQA_ERR_ALIGN = 9,       /* a pointer is not aligned to its element size       */
+    GQA_ERR_HIP = 10,        /* the HIP runtime reported an error at launch        */
+    GQA_ERR_SCALE = 11       /* scale is NaN or infinite                           */
+} gqa_status;
+
+typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
+
+#define GQA_NO_WINDOW (-1)
+#define GQA_MAX_HEAD_DIM 256
+
+/* Which kernel family a call would run (for tests and reports). */
+typedef enum {
+    GQA_KERNEL_NONE = 0,       /* nothing to launch (empty batch or no rows)      */
+    GQA_KERNEL_GENERIC = 1,    /* one wavefront per row and KV group, fp32 or bf16 */
+    GQA_KERNEL_DECODE_SPLIT = 2, /* bf16 MFMA split-K decode + LSE combine          */
+    GQA_KERNEL_PREFILL_MFMA = 3  /* bf16 MFMA flash prefill                         */
+} gqa_kernel;
+
+/*
+ * Causal prefill.  "Share key/value heads and make context explicit",
+ * "Intersect the window with the context already permitted" (active lengths,
+ * window rule) and "Give each query head an explicit shared KV head" (scores,
+ * permitted-set softmax, value mix, merged heads).
+ *
+ *   q        [B, Hq, T, d]   queries of cells 0..T-1 (already rotated)
+ *   k_cache  [B, Hkv, C, d]  keys; cells 0..n_b-1 are read
+ *   v_cache  [B, Hkv, C, d]  values
+ *   out      [B, T, Hq, d]   = merged rows [B, T, Hq*d]; rows t >= n_b are 0
+ *   seqlens  [B] int32 active lengths n_b (0 <= n_b <= T), or NULL for n_b = T
+ *   Requires 0 <= T <= C.  B == 0 or T == 0 is a no-op returning GQA_OK.
+ */
+int gqa_prefill(const void *q, const void *k_cache, const void *v_cache, void *out,
+                const int32_t *seqlens, int32_t B, int32_t T, int32_t C, int32_t Hq,
+                int32_t Hkv, int32_t d, int32_t window, float scale, int32_t dtype,
+                void *stream);
+
+/*
+ * Workspace size in bytes that gqa_decode needs for these arguments (0 when
+ * the chosen kernel needs none).  Depends only on the arguments.  Returns 0
+ * for arguments gqa_decode would refuse.
+ */
+size_t gqa_decode_workspace_bytes(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
+                                  int32_t window, int32_t dtype);
+
+/*
+ * Single-token decode against a cached prefix.  "Share key/value heads and
+ * make context explicit", "Extend the existing full and cached attention
+ * paths" (the new query reads every permitted earlier key plus its own
+ * candidate key) and "GQA, FlashAttention and the KV cache", "The important
+ * mask bug with a cache" (the one new query sees all previous keys).
+ *
+ *   q        [B, Hq, d]      the new token's queries
+ *   k_cache  [B, Hkv, C, d]  keys; the caller has already written the new
+ *                            token's key and value at cell n_b - 1
+ *   v_cache  [B, Hkv, C, d]
+ *   out      [B, Hq, d]      = merged row [B, Hq*d]
+ *   seqlens  [B] int32 n_b = cells in use including the new one
+ *            (0 <= n_b <= C; n_b == 0 gives a zero row), or NULL for n_b = C
+ *   The query sits at cell n_b - 1 and reads cells max(0, n_b - w)..n_b - 1
+ *   (all n_b cells without a window).
+ *   workspace: device scratch of at least gqa_decode_workspace_bytes(...)
+ *   bytes, 256-byte aligned (may be NULL when that size is 0).  Its contents
+ *   on entry do not matter; concurrent calls must not share one workspace.
+ *   B == 0 is a no-op returning GQA_OK.
+ */
+int gqa_decode(const void *q, const void *k_cache, const void *v_cache, void *out,
+               const int32_t *seqlens, int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
+               int32_t d, int32_t window, float scale, int32_t dtype, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/*
+ * Index-set records: the same kernels, instantiated to also write, for every
+ * output row, five int32 values {KV head read, lowest key folded in, highest
+ * key folded in, number of keys folded in, XOR of the folded key indices}
+ * counted at the point of accumulation ({g, -1, -1, 0, 0} for an inactive
+ * row).  records is [B, T, Hq, 5] for prefill and [B, Hq, 5] for decode.
+ * Everything else is as for gqa_prefill / gqa_decode, and out is written too.
+ */
+int gqa_prefill_records(const void *q, const void *k_cache, const void *v_cache, void *out,
+                        const int32_t *seqlens, int32_t B, int32_t T, int32_t C, int32_t Hq,
+                        int32_t Hkv, int32_t d, int32_t window, float scale, int32_t dtype,
+                        int32_t *records, void *stream);
+int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, void *out,
+                       const int32_t *seqlens, int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
+                       int32_t d, int32_t window, float scale, int32_t dtype, void *workspace,
+                       size_t workspace_bytes, int32_t *records, void *stream);
+
+/* The kernel family gqa_prefill / gqa_decode would launch for these arguments
+ * (GQA_KERNEL_NONE for a no-op or a refused call).  Alignment is assumed. */
+int gqa_prefill_kernel(int32_t B, int32_t T, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
+                       int32_t window, int32_t dtype);
+int gqa_decode_kernel(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t d, int32_t window,
+                      int32_t dtype);
+
+/*
+ * Host helpers (no device work).
+ *
+ * gqa_kv_head_for_query: floor(h / (Hq / Hkv)), or -1 when Hkv <= 0, Hq <= 0,
+ *   Hq % Hkv != 0 or h is outside 0..Hq-1 (kv_head_for_query in "Extend the
+ *   existing full and cached attention paths").
+ * gqa_window_start: max(s, t - (w - 1)) with the subtraction saturating at 0,
+ *   or -1 when w == 0, s > t or an argument is negative (causal_window_start,
+ *   same section).
+ * gqa_kv_cache_bytes: 2 * L * B * T * Hkv * d * e, the K plus V payload of a
+ *   cache ("GQA, FlashAttention and the KV cache", "Computing the cache
+ *   requirement"); returns GQA_OK and writes *bytes, GQA_ERR_OVERFLOW if the
+ *   product does not fit in 64 bits, GQA_ERR_NULL if bytes is NULL.
+ * gqa_status_string: a static message for a status code.
+ */
+int32_t gqa_kv_head_for_query(int32_t h, int32_t Hq, int32_t Hkv);
+int64_t gqa_window_start(int64_t t, int64_t seg_start, int64_t w);
+int gqa_kv_cache_bytes(uint64_t L, uint64_t B, uint64_t T, uint64_t Hkv, uint64_t d, uint64_t e,
+                       uint64_t *bytes);
+const char *gqa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GQA_H */

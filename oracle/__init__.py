@@ -61,6 +61,13 @@ def lib():
     return _lib
 
 
+def threads() -> int:
+    """OpenMP threads the oracle's parallel loops use in this process."""
+    f = lib().omp_get_max_threads
+    f.restype = ctypes.c_int
+    return int(f())
+
+
 class OracleError(RuntimeError):
     def __init__(self, code: int):
         super().__init__(f"oracle refused the call (code {code})")

@@ -1,0 +1,346 @@
+"""Parity of the HIP kernels (through the C-ABI) with the fp64 oracle.
+
+Tolerances: max-abs error 1e-5 for fp32 storage and 2e-2 for bf16 storage
+with fp32 arithmetic.  Integer index sets (KV head read, lowest and highest
+key, key count, XOR of the keys folded in) must match exactly.  Both sides
+always see the same input bits: the oracle gets the stored fp32/bf16 values
+widened to fp64.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_kv_cache_02_amd as gqa
+import oracle
+from gqa_kv_cache_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+F32_TOL = 1e-5
+BF16_TOL = 2e-2
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+def _tol(dtype):
+    return F32_TOL if dtype == torch.float32 else BF16_TOL
+
+
+def _maxerr(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gqa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def run_prefill(q, k, v, seqlens=None, window=None, scale=None, records=False):
+    B, hq, T, d = q.shape
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    rec = torch.full((B, T, hq, 5), -7, dtype=torch.int32, device=DEV) if records else None
+    out = gqa.prefill(q, k, v, seqlens=sl, window=window, scale=scale, records=rec)
+    torch.cuda.synchronize()
+    return out, rec
+
+
+def run_decode(q, k, v, seqlens=None, window=None, scale=None, records=False, workspace=None):
+    B, hq, d = q.shape
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    rec = torch.full((B, hq, 5), -7, dtype=torch.int32, device=DEV) if records else None
+    out = gqa.decode(q, k, v, seqlens=sl, window=window, scale=scale, records=rec,
+                     workspace=workspace)
+    torch.cuda.synchronize()
+    return out, rec
+
+
+# ---------------------------------------------------------------------------
+# the pages' worked example, through every kernel family that can run it
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_worked_example(dtype):
+    q, k, v = synth.fixture_4token(dtype, DEV)
+    expect = {None: [2.5, 0, 2.5, 0, 0, 25, 0, 25], 2: [3.5, 0, 3.5, 0, 0, 35, 0, 35]}
+    for w, row in expect.items():
+        out, rec = run_prefill(q, k, v, window=w, records=True)
+        assert _np(out)[0, 3].reshape(-1).tolist() == row
+        assert _np(rec)[0, 3, :, 0].tolist() == [0, 0, 1, 1]
+        # decode of the last cell gives the same merged row
+        dq = q[:, :, 3].contiguous()
+        dout, _ = run_decode(dq, k, v, window=w)
+        assert _np(dout)[0].reshape(-1).tolist() == row
+
+
+def test_worked_example_fast_paths_d64():
+    # the same zero-Q/K fixture embedded in d = 64 so the bf16 MFMA kernels run it
+    q, k, v = synth.fixture_4token(torch.float32, "cpu")
+    pad = lambda t: torch.nn.functional.pad(t, (0, 62)).to(torch.bfloat16).to(DEV).contiguous()
+    q, k, v = pad(q), pad(k), pad(v)
+    assert gqa.decode_kernel(1, 4, 4, 2, 64) == "decode_split"
+    for w, row in {None: [2.5, 0, 2.5, 0, 0, 25, 0, 25], 2: [3.5, 0, 3.5, 0, 0, 35, 0, 35]}.items():
+        out, _ = run_prefill(q, k, v, window=w)
+        assert _np(out)[0, 3, :, :2].reshape(-1).tolist() == row
+        dout, _ = run_decode(q[:, :, 3].contiguous(), k, v, window=w)
+        assert _np(dout)[0, :, :2].reshape(-1).tolist() == row
+
+
+# ---------------------------------------------------------------------------
+# small prefill configuration (fp32) and sweeps
+# ---------------------------------------------------------------------------
+
+def test_prefill_f32_small_config():
+    cfg = synth.CONFIGS["prefill_f32_small"]
+    q, k, v = synth.prefill_inputs(cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"],
+                                   torch.float32, cfg["seed"], DEV)
+    for w in cfg["windows"]:
+        out, rec = run_prefill(q, k, v, window=w, records=True)
+        ref, _, rrec = oracle.prefill(_np(q), _np(k), _np(v), window=w, want_records=True)
+        assert _maxerr(_np(out), ref) <= F32_TOL
+        assert np.array_equal(_np(rec).astype(np.int32), rrec)
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("d", [1, 2, 8, 64, 96, 128, 256])
+def test_prefill_sweep(dtype, d):
+    B, T, C = 2, 37, 41
+    for hq, hkv in ((4, 4), (4, 2), (4, 1), (6, 3), (16, 2)):
+        q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, dtype, 100 + d + hq, DEV, C=C)
+        for w in (None, 1, 5, 16, 17, 64):
+            seqlens = [T, 23]
+            out, rec = run_prefill(q, k, v, seqlens=seqlens, window=w, records=True)
+            ref, _, rrec = oracle.prefill(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
+                                          want_records=True)
+            err = _maxerr(_np(out), ref)
+            assert err <= _tol(dtype), (hq, hkv, w, err)
+            assert np.array_equal(_np(rec).astype(np.int32), rrec), (hq, hkv, w)
+            assert not _np(out)[1, 23:].any()
+
+
+# ---------------------------------------------------------------------------
+# decode: split kernel (bf16, d in {64,128}) and generic kernel
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_decode_split_sweep(d):
+    C = 700
+    seqlens = [700, 513, 129, 128, 127, 33, 32, 1, 0]
+    B = len(seqlens)
+    for hq, hkv in ((8, 8), (8, 2), (8, 1), (6, 2), (32, 8), (32, 1)):
+        assert gqa.decode_kernel(B, C, hq, hkv, d) == "decode_split"
+        q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 7 + hq + hkv, DEV)
+        for w in (None, 1, 31, 32, 33, 100, 512, 10 ** 6):
+            out, rec = run_decode(q, k, v, seqlens=seqlens, window=w, records=True)
+            ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
+                                         want_records=True)
+            err = _maxerr(_np(out), ref)
+            assert err <= BF16_TOL, (hq, hkv, w, err)
+            assert np.array_equal(_np(rec).astype(np.int32), rrec), (hq, hkv, w)
+            assert not _np(out)[-1].any()
+
+
+@pytest.mark.parametrize("dtype,d", [(torch.float32, 8), (torch.float32, 128), (torch.bfloat16, 40),
+                                     (torch.float32, 256)])
+def test_decode_generic_sweep(dtype, d):
+    C = 90
+    seqlens = [90, 45, 1, 0]
+    B = len(seqlens)
+    for hq, hkv in ((4, 2), (8, 1), (3, 3), (24, 2)):
+        assert gqa.decode_kernel(B, C, hq, hkv, d, dtype=dtype) == "generic"
+        q, k, v = synth.decode_inputs(B, C, hq, hkv, d, dtype, 3 + d + hq, DEV)
+        for w in (None, 1, 7, 200):
+            out, rec = run_decode(q, k, v, seqlens=seqlens, window=w, records=True)
+            ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
+                                         want_records=True)
+            assert _maxerr(_np(out), ref) <= _tol(dtype), (hq, hkv, w)
+            assert np.array_equal(_np(rec).astype(np.int32), rrec)
+
+
+def test_decode_equals_prefill_row():
+    # the full/cached invariant on the device: decode at n equals prefill row n-1
+    B, hq, hkv, T, d = 2, 8, 2, 150, 128
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, 77, DEV)
+    for w in (None, 20):
+        full, _ = run_prefill(q, k, v, window=w)
+        for n in (1, 2, 31, 32, 33, 64, 100, 150):
+            dec, _ = run_decode(q[:, :, n - 1].contiguous(), k, v, seqlens=[n] * B, window=w)
+            assert _maxerr(_np(dec), _np(full[:, n - 1])) <= BF16_TOL
+
+
+def test_zero_qk_probe_index_sets():
+    # Q = K = 0 gives equal weights; with V channels [1, g, j, j^2] the outputs
+    # are 1, the KV head, the mean key index and the mean of j^2 over the
+    # permitted set -- exact in fp32 arithmetic and bf16 storage for j <= 256.
+    for d in (64, 128):
+        B, hq, hkv, C = 3, 8, 2, 256
+        q = torch.zeros((B, hq, d), dtype=torch.bfloat16, device=DEV)
+        k = torch.zeros((B, hkv, C, d), dtype=torch.bfloat16, device=DEV)
+        v = torch.zeros((B, hkv, C, d), dtype=torch.float32)
+        j = torch.arange(C, dtype=torch.float32)
+        for g in range(hkv):
+            v[:, g, :, 0] = 1.0
+            v[:, g, :, 1] = float(g)
+            v[:, g, :, 2] = j
+        v = v.to(torch.bfloat16).to(DEV)
+        seqlens = [256, 100, 17]
+        for w in (None, 1, 31, 32, 33, 64):
+            out, _ = run_decode(q, k, v, seqlens=seqlens, window=w)
+            o = _np(out)
+            for b, n in enumerate(seqlens):
+                lo = 0 if w is None else max(0, n - w)
+                for h in range(hq):
+                    assert o[b, h, 0] == 1.0
+                    assert o[b, h, 1] == float(h // (hq // hkv))
+                    mean = (lo + n - 1) / 2.0
+                    assert abs(o[b, h, 2] - mean) <= abs(mean) * 2 ** -8, (w, b, h)
+
+
+def test_dirty_workspace_and_side_stream():
+    B, C, hq, hkv, d = 4, 1000, 16, 4, 128
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 5, DEV)
+    need = gqa.decode_workspace_bytes(B, C, hq, hkv, d)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN patterns everywhere
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = gqa.decode(q, k, v, seqlens=torch.tensor([1000, 999, 3, 500], dtype=torch.int32,
+                                                       device=DEV), workspace=ws)
+    s.synchronize()
+    ref, _, _ = oracle.decode(_np(q), _np(k), _np(v), seqlens=[1000, 999, 3, 500])
+    assert _maxerr(_np(out), ref) <= BF16_TOL
+
+
+def test_refused_call_leaves_output_untouched():
+    q, k, v = synth.decode_inputs(2, 64, 8, 2, 128, torch.bfloat16, 1, DEV)
+    out = torch.full((2, 8, 128), 3.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gqa.GQAError) as e:
+        gqa.decode(q, k, v, window=0, out=out)
+    assert e.value.status == 3
+    torch.cuda.synchronize()
+    assert (out == 3.0).all()
+    qp = torch.zeros((1, 4, 8, 64), dtype=torch.bfloat16, device=DEV)
+    kp = torch.zeros((1, 2, 4, 64), dtype=torch.bfloat16, device=DEV)  # C = 4 < T = 8
+    outp = torch.full((1, 8, 4, 64), 5.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gqa.GQAError) as e:
+        gqa.prefill(qp, kp, kp, out=outp)
+    assert e.value.status == 6
+    torch.cuda.synchronize()
+    assert (outp == 5.0).all()
+
+
+def test_empty_inputs():
+    q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((0, 2, 16, 128), dtype=torch.bfloat16, device=DEV)
+    assert gqa.decode(q, k, k).shape == (0, 8, 128)
+    qp = torch.zeros((1, 8, 0, 128), dtype=torch.bfloat16, device=DEV)
+    kp = torch.zeros((1, 2, 16, 128), dtype=torch.bfloat16, device=DEV)
+    assert gqa.prefill(qp, kp, kp).shape == (1, 0, 8, 128)
+    # a decode cache with zero capacity gives zero rows
+    q1 = torch.ones((2, 4, 64), dtype=torch.bfloat16, device=DEV)
+    k0 = torch.zeros((2, 2, 0, 64), dtype=torch.bfloat16, device=DEV)
+    out, _ = run_decode(q1, k0, k0)
+    assert not _np(out).any()
+
+
+# ---------------------------------------------------------------------------
+# full-size configurations: sampled rows against the oracle, properties for all
+# ---------------------------------------------------------------------------
+
+def _convex_bounds_ok(out, v, hq, hkv, lo, hi):
+    """Each output coordinate is a convex combination of the permitted values:
+    it lies between their minimum and maximum (checked for every row)."""
+    r = hq // hkv
+    for b in range(out.shape[0]):
+        vs = v[b, :, lo[b]:hi[b] + 1].float()            # [Hkv, n, d]
+        vmin = vs.amin(dim=1).repeat_interleave(r, dim=0)  # [Hq, d]
+        vmax = vs.amax(dim=1).repeat_interleave(r, dim=0)
+        o = out[b].float()
+        if not bool(((o >= vmin - BF16_TOL) & (o <= vmax + BF16_TOL)).all()):
+            return False
+    return True
+
+
+def _decode_full_check(B, C, hq, hkv, d, seqlens, window, seed, sample_b):
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, seed, DEV)
+    out, rec = run_decode(q, k, v, seqlens=seqlens, window=window, records=True)
+    assert bool(torch.isfinite(out.float()).all())
+    # index sets of every row, from the oracle on zero inputs of width 1
+    _, _, rrec = oracle.decode(np.zeros((B, hq, 1)), np.zeros((B, hkv, C, 1)),
+                               np.zeros((B, hkv, C, 1)), seqlens=seqlens, window=window,
+                               want_records=True)
+    assert np.array_equal(_np(rec).astype(np.int32), rrec)
+    # values of sampled batch rows, one by one
+    for b in sample_b:
+        ref, _, _ = oracle.decode(_np(q[b:b + 1]), _np(k[b:b + 1]), _np(v[b:b + 1]),
+                                  seqlens=[seqlens[b]], window=window)
+        assert _maxerr(_np(out[b:b + 1]), ref) <= BF16_TOL, b
+    lo = [0 if window is None else max(0, n - window) for n in seqlens]
+    hi = [n - 1 for n in seqlens]
+    assert _convex_bounds_ok(out, v, hq, hkv, lo, hi)
+
+
+def test_full_decode_b8_hq32_hkv8_d128_n8000():
+    cfg = synth.CONFIGS["decode_b8_hq32_hkv8_d128_n8000"]
+    _decode_full_check(cfg["B"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"], [cfg["n"]] * cfg["B"],
+                       cfg["window"], cfg["seed"], sample_b=(0, 5, 7))
+
+
+@pytest.mark.parametrize("hkv", [8, 2, 1])
+def test_full_decode_endpoint_sweep(hkv):
+    cfg = synth.CONFIGS["decode_sweep_b16_hq8_d128_n8000"]
+    _decode_full_check(cfg["B"], cfg["C"], cfg["Hq"], hkv, cfg["d"], [cfg["n"]] * cfg["B"],
+                       cfg["window"], cfg["seed"] + hkv, sample_b=(0, 15))
+
+
+def test_full_decode_endpoints_equal_explicit_repeat():
+    # MQA and GQA equal MHA run on repeat_interleave'd K/V (the same kernels,
+    # Hkv = Hq): the grouping never changes the result beyond rounding.
+    B, C, hq, d = 16, 8000, 8, 128
+    for hkv in (1, 2):
+        q, kk, vv = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 4242 + hkv, DEV)
+        grouped, _ = run_decode(q, kk, vv)
+        rep_k = kk.repeat_interleave(hq // hkv, dim=1).contiguous()
+        rep_v = vv.repeat_interleave(hq // hkv, dim=1).contiguous()
+        mha, _ = run_decode(q, rep_k, rep_v)
+        err = _maxerr(_np(grouped), _np(mha))
+        assert err <= BF16_TOL
+        if hkv == 2:  # a tiled repeat pairs heads with the wrong KV head
+            tiled, _ = run_decode(q, kk.repeat(1, hq // hkv, 1, 1).contiguous(),
+                                  vv.repeat(1, hq // hkv, 1, 1).contiguous())
+            wrong = _maxerr(_np(grouped), _np(tiled))
+            assert wrong > 2 * BF16_TOL and wrong > 20 * err
+
+
+def test_full_decode_ragged_window():
+    cfg = synth.CONFIGS["decode_ragged_b32_hq8_hkv2_d64_w4096"]
+    lo, hi = cfg["n"]
+    seqlens = synth.ragged_lengths(cfg["B"], lo, hi, cfg["seed"]).tolist()
+    _decode_full_check(cfg["B"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"], seqlens,
+                       cfg["window"], cfg["seed"], sample_b=(0, 1, 17, 31))
+
+
+def test_full_prefill_t4096_sampled_rows():
+    cfg = synth.CONFIGS["prefill_b1_t4096_hq32_hkv8_d128"]
+    B, T, hq, hkv, d = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, cfg["seed"], DEV)
+    out, rec = run_prefill(q, k, v, records=True)
+    o = _np(out)
+    assert np.isfinite(o).all()
+    r = _np(rec).astype(np.int64)
+    t = np.arange(T)[None, :, None]
+    h = np.arange(hq)[None, None, :]
+    assert (r[..., 0] == h // (hq // hkv)).all()
+    assert (r[..., 1] == 0).all() and (r[..., 2] == t).all() and (r[..., 3] == t + 1).all()
+    # sampled rows: the oracle's decode at n = t + 1 is prefill row t
+    kn, vn = _np(k), _np(v)
+    for tt in (0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 4094, 4095):
+        ref, _, _ = oracle.decode(_np(q[:, :, tt]), kn, vn, seqlens=[tt + 1])
+        assert _maxerr(o[:, tt], ref) <= BF16_TOL, tt
