@@ -81,9 +81,7 @@ bool fast_aligned(const void *q, const void *k, const void *v, const void *out) 
 }
 
 int prefill_kernel_for(int32_t d, int32_t dtype) {
-    (void)d;
-    (void)dtype;
-    return GQA_KERNEL_GENERIC;
+    return fast_shape(d, dtype) ? GQA_KERNEL_PREFILL_MFMA : GQA_KERNEL_GENERIC;
 }
 
 int decode_kernel_for(int32_t d, int32_t dtype) {
@@ -114,14 +112,16 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
             return GQA_ERR_ALIGN;
     }
     const int r = Hq / Hkv;
-    if (B > kMaxGridYZ || (int64_t)Hkv * ((r + 7) / 8) > kMaxGridYZ)
-        return GQA_ERR_SHAPE;
-
     Problem p{q, k, v, out, seqlens, want_records ? records : nullptr,
               B, T, C, Hq, Hkv, d, window, scale, dtype, false};
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (prefill_kernel_for(d, dtype) == GQA_KERNEL_PREFILL_MFMA && fast_aligned(q, k, v, out))
+    if (prefill_kernel_for(d, dtype) == GQA_KERNEL_PREFILL_MFMA && fast_aligned(q, k, v, out)) {
+        if (!gqa::prefill_grid_ok(B, T, Hq, Hkv))
+            return GQA_ERR_SHAPE;
         return status_of(gqa::launch_prefill_mfma(p, s));
+    }
+    if (B > kMaxGridYZ || (int64_t)Hkv * ((r + 7) / 8) > kMaxGridYZ)
+        return GQA_ERR_SHAPE;
     return status_of(gqa::launch_generic(p, s));
 }
 

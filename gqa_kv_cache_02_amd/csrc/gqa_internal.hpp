@@ -44,5 +44,6 @@ hipError_t launch_generic(const Problem &p, hipStream_t stream);
 hipError_t launch_decode_split(const Problem &p, const DecodePlan &plan, void *workspace,
                                hipStream_t stream);
 hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream);
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv);
 
 } // namespace gqa

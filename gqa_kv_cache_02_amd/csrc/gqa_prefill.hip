@@ -1,11 +1,358 @@
-// gqa_prefill.hip -- bf16 MFMA flash prefill (not yet enabled).
+// gqa_prefill.hip -- bf16 causal prefill with matrix cores (MFMA), in the
+// blockwise online-softmax form ("GQA, FlashAttention and the KV cache",
+// section "FlashAttention": blocks and a numerically stable running
+// normalisation give the dense result without materialising the score
+// matrix; the dense pairwise work remains).
+//
+// Work decomposition.  A workgroup owns one batch row b, one KV group g and
+// one block of query rows, and runs up to 4 wavefronts: `hpw` query heads of
+// group g times `rb` blocks of 32 rows (hpw * rb <= 4).  All its wavefronts
+// read the same K/V tiles, which are staged once in LDS per workgroup -- the
+// r query heads that share a KV head ("Share key/value heads and make context
+// explicit", "Give each query head an explicit shared KV head") never cause a
+// second read or a repeated copy.
+//
+// Per 64-key tile and wavefront (32 query rows):
+//   S^T[64 keys x 32 rows] = K[64 x d] . Q^T[d x 32]     (MFMA 32x32x16 bf16)
+//   mask (diagonal, window edge and padded rows only), base-2 online softmax
+//   O^T[d x 32] += V^T[d x 64] . P^T[64 x 32]            (MFMA 32x32x16 bf16)
+// The transposed products keep every row's running max and sum in the two
+// lanes that own the row (l and l ^ 32).  V^T comes straight out of the
+// natural-layout LDS tile with ds_read_b64_tr_b16.  Tiles entirely above the
+// causal diagonal or entirely before every row's window start are never
+// visited; only diagonal and window-edge tiles are masked ("Intersect the
+// window with the context already permitted").
+#include <limits.h>
+
 #include "gqa_common.hpp"
 #include "gqa_internal.hpp"
 
 namespace gqa {
 
+constexpr int kPBN = 64;   // keys per K/V tile
+constexpr int kPRows = 32; // query rows per wavefront
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+struct PrefillArgs {
+    const uint16_t *q;
+    const uint16_t *k;
+    const uint16_t *v;
+    uint16_t *out;
+    const int32_t *seqlens;
+    int32_t *records;
+    int T, C, Hq, Hkv, window, r, hpw, rb, nhc, nqb;
+    float scale_log2;
+};
+
+template <int D> struct PrefillSmem {
+    static constexpr int LDK = D + 8; // padded row (u16) of the K and V tiles
+    static constexpr int kTile = kPBN * LDK;
+};
+
+__device__ __forceinline__ s16x4 ds_read_tr(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+}
+
+template <int D, bool kRecord>
+__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+    constexpr int KS = D / 16;   // 16-feature k-steps of Q.K (32x32x16)
+    constexpr int DB = D / 32;   // 32-column blocks of P.V
+    constexpr int LDK = PrefillSmem<D>::LDK;
+    constexpr int CPR = D / 8;   // 16-byte chunks per key row
+    constexpr int LPT = kPBN * CPR / 256; // 16-byte loads per thread per tensor
+
+    __shared__ __attribute__((aligned(16))) uint16_t ks[PrefillSmem<D>::kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[PrefillSmem<D>::kTile];
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int nwaves = a.hpw * a.rb;
+
+    const int b = blockIdx.z;
+    const int g = blockIdx.y / a.nhc;
+    const int hc = blockIdx.y % a.nhc;
+    const int qblk = a.nqb - 1 - static_cast<int>(blockIdx.x); // heaviest blocks first
+    const int rows_wg = kPRows * a.rb;
+    const int q0 = qblk * rows_wg;
+
+    const int nb = a.seqlens ? a.seqlens[b] : a.T;
+    const bool wave_on = wave < nwaves;
+    const int hh = wave % a.hpw;            // head within the workgroup
+    const int rsub = wave / a.hpw;          // 32-row block within the workgroup
+    const int h = g * a.r + hc * a.hpw + hh;
+    const int r0 = q0 + rsub * kPRows;
+    const int my_row = r0 + (lane & 31);
+
+    // Key range the workgroup needs: from the earliest row's window start to
+    // its last active row.
+    const int wg_last = min(q0 + rows_wg, min(nb, a.T)) - 1;
+    const int64_t out_stride = (int64_t)a.Hq * D; // between cells in [B,T,Hq,D]
+
+    if (wg_last < q0) {
+        // no active row: the whole block is padding, write zeros
+        if (wave_on) {
+            for (int i = lane; i < kPRows * (D / 4); i += 64) {
+                const int row = r0 + i / (D / 4);
+                const int c4 = (i % (D / 4)) * 4;
+                if (row < a.T) {
+                    uint16_t *o = a.out + ((int64_t)b * a.T + row) * out_stride + (int64_t)h * D + c4;
+                    *reinterpret_cast<uint2 *>(o) = uint2{0u, 0u};
+                    if (kRecord && c4 == 0) {
+                        int32_t *rec = a.records + (((int64_t)b * a.T + row) * a.Hq + h) * 5;
+                        rec[0] = g; rec[1] = -1; rec[2] = -1; rec[3] = 0; rec[4] = 0;
+                    }
+                }
+            }
+        }
+        return;
+    }
+    const int wg_lo = window_lo(q0, a.window);
+    const int tile_lo = wg_lo / kPBN;
+    const int tile_hi = wg_last / kPBN;
+
+    // The wavefront's own key range.
+    const int w_last = min(r0 + kPRows, min(nb, a.T)) - 1; // < r0 when all rows padded
+    const int w_lo = window_lo(r0, a.window);
+    const int w_lo_last = window_lo(r0 + kPRows - 1, a.window);
+
+    // Q^T operand, kept for the whole loop: lane l holds row r0 + (l & 31),
+    // features s*16 + 8*(l >> 5) .. +8.
+    bf16x8 qb[KS];
+    {
+        const bool ok = wave_on && my_row < a.T;
+        const uint16_t *qrow = a.q + (((int64_t)b * a.Hq + h) * a.T + (ok ? my_row : 0)) * D;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            if (ok)
+                qb[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 16 + 8 * (lane >> 5));
+            else
+                qb[s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+    }
+
+    const int64_t kv_off = ((int64_t)b * a.Hkv + g) * (int64_t)a.C * D;
+    const uint16_t *kbase = a.k + kv_off;
+    const uint16_t *vbase = a.v + kv_off;
+
+    f32x16 oacc[DB];
+#pragma unroll
+    for (int i = 0; i < DB; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            oacc[i][e] = 0.f;
+    float m = -INFINITY; // running max of this lane's row (base-2 scaled)
+    float lsum = 0.f;    // this lane's share of the running sum
+    int r_cnt = 0, r_xor = 0, r_lo = INT_MAX, r_hi = -1;
+
+    // Register staging of one K/V tile: thread loads chunk c = tid + 256*i.
+    uint4 kreg[LPT], vreg[LPT];
+    auto load_tile = [&](int tile) {
+        const int j0 = tile * kPBN;
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int c = tid + 256 * i;
+            const int key = j0 + c / CPR;
+            const int col = (c % CPR) * 8;
+            if (key <= wg_last) {
+                kreg[i] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)key * D + col);
+                vreg[i] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)key * D + col);
+            } else {
+                kreg[i] = uint4{0u, 0u, 0u, 0u};
+                vreg[i] = uint4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+
+    load_tile(tile_lo);
+    for (int tile = tile_lo; tile <= tile_hi; ++tile) {
+        __syncthreads(); // every wavefront is done with the previous tile
+#pragma unroll
+        for (int i = 0; i < LPT; ++i) {
+            const int c = tid + 256 * i;
+            const int row = c / CPR;
+            const int col = (c % CPR) * 8;
+            *reinterpret_cast<uint4 *>(ks + row * LDK + col) = kreg[i];
+            *reinterpret_cast<uint4 *>(vs + row * LDK + col) = vreg[i];
+        }
+        __syncthreads();
+        if (tile < tile_hi)
+            load_tile(tile + 1); // in flight while this tile is computed
+
+        const int j0 = tile * kPBN;
+        // Skip tiles that lie wholly outside this wavefront's rows' ranges.
+        if (!wave_on || w_last < r0 || j0 > w_last || j0 + kPBN - 1 < w_lo)
+            continue;
+        const bool full = (j0 + kPBN - 1 <= r0) && (j0 >= w_lo_last) && (r0 + kPRows - 1 <= w_last);
+
+        // S^T = K . Q^T for two 32-key blocks.
+        f32x16 sacc[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                sacc[kb][e] = 0.f;
+            const uint16_t *krow = ks + (kb * 32 + (lane & 31)) * LDK + 8 * (lane >> 5);
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(krow + s * 16);
+                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[kb], 0, 0, 0);
+            }
+        }
+
+        // Scale, mask, running max.  Lane l holds row r0 + (l & 31) and keys
+        // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.
+        const int qq = lane >> 5;
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                float x = sacc[kb][v] * a.scale_log2;
+                if (!full) {
+                    const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
+                    const bool keep = (j <= my_row) && (my_row <= w_last) &&
+                                      (j >= window_lo(my_row, a.window));
+                    x = keep ? x : -INFINITY;
+                }
+                sacc[kb][v] = x;
+                tmax = fmaxf(tmax, x);
+            }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m, tmax);
+        const float msafe = (mn == -INFINITY) ? 0.f : mn;
+        const float alpha = exp2f(m - msafe);
+        m = mn;
+        float psum = 0.f;
+        bf16x8 pb[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float p = exp2f(sacc[kb][v] - msafe);
+                psum += p;
+                pb[kb][v / 8][v % 8] = static_cast<short>(f32_to_bf16(p));
+                if (kRecord && sacc[kb][v] != -INFINITY) { // a permitted cell
+                    const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
+                    r_cnt += 1;
+                    r_xor ^= j;
+                    r_lo = min(r_lo, j);
+                    r_hi = max(r_hi, j);
+                }
+            }
+        lsum = fmaf(lsum, alpha, psum);
+#pragma unroll
+        for (int i = 0; i < DB; ++i)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                oacc[i][e] *= alpha;
+
+        // O^T += V^T . P^T.  For key block kb and k-step st, P^T k-slot
+        // 8*(l>>5) + e is key kb*32 + 16*st + 8*(e/4) + 4*(l>>5) + e%4, so V^T
+        // needs two runs of 4 consecutive keys per lane: a transposing LDS read
+        // per run.  In each 16-lane group, lane j supplies row k0 + j/4,
+        // columns c0 + 4*(j%4) .. +3 and receives column c0 + (lane & 15).
+        const int gl = lane & 15;
+        const int cgrp = (lane >> 4) & 1; // which 16 columns of the 32
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+                const int k0 = kb * 32 + 16 * st + 4 * qq;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int c0 = db * 32 + 16 * cgrp + 4 * (gl & 3);
+                    const s16x4 lo4 = ds_read_tr(vs + (k0 + (gl >> 2)) * LDK + c0);
+                    const s16x4 hi4 = ds_read_tr(vs + (k0 + 8 + (gl >> 2)) * LDK + c0);
+                    const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][st], oacc[db], 0, 0, 0);
+                }
+            }
+    }
+
+    if (!wave_on)
+        return;
+    lsum += __shfl_xor(lsum, 32, 64);
+    if (kRecord) {
+        r_cnt += __shfl_xor(r_cnt, 32, 64);
+        r_xor ^= __shfl_xor(r_xor, 32, 64);
+        r_lo = min(r_lo, __shfl_xor(r_lo, 32, 64));
+        r_hi = max(r_hi, __shfl_xor(r_hi, 32, 64));
+    }
+    if (my_row >= a.T)
+        return;
+    const bool active = my_row < nb;
+    const float inv = (active && lsum > 0.f) ? 1.f / lsum : 0.f;
+    uint16_t *orow = a.out + ((int64_t)b * a.T + my_row) * out_stride + (int64_t)h * D;
+    const int qq = lane >> 5;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int v4 = 0; v4 < 4; ++v4) {
+            const int col = db * 32 + 8 * v4 + 4 * qq;
+            uint2 pk;
+            pk.x = pack_bf16x2(oacc[db][4 * v4 + 0] * inv, oacc[db][4 * v4 + 1] * inv);
+            pk.y = pack_bf16x2(oacc[db][4 * v4 + 2] * inv, oacc[db][4 * v4 + 3] * inv);
+            *reinterpret_cast<uint2 *>(orow + col) = pk;
+        }
+    if (kRecord && qq == 0) {
+        int32_t *rec = a.records + (((int64_t)b * a.T + my_row) * a.Hq + h) * 5;
+        rec[0] = g;
+        if (active) {
+            rec[1] = r_lo; rec[2] = r_hi; rec[3] = r_cnt; rec[4] = r_xor;
+        } else {
+            rec[1] = -1; rec[2] = -1; rec[3] = 0; rec[4] = 0;
+        }
+    }
+}
+
+// Heads per workgroup: the largest divisor of r that is at most 4; the
+// remaining wavefronts take further 32-row blocks of the same heads.
+static void prefill_shape(int r, int *hpw, int *rb) {
+    int best = 1;
+    for (int x = 4; x >= 1; --x)
+        if (r % x == 0) {
+            best = x;
+            break;
+        }
+    *hpw = best;
+    *rb = (4 % best == 0) ? 4 / best : 1;
+}
+
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv) {
+    int hpw, rb;
+    prefill_shape(Hq / Hkv, &hpw, &rb);
+    const int64_t y = (int64_t)Hkv * ((Hq / Hkv) / hpw);
+    return B <= 65535 && y <= 65535 && T >= 0;
+}
+
+template <int D, bool kRecord>
+static hipError_t launch_p(const PrefillArgs &a, dim3 grid, hipStream_t s) {
+    prefill_mfma_kernel<D, kRecord><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
 hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream) {
-    return launch_generic(p, stream);
+    PrefillArgs a;
+    a.q = static_cast<const uint16_t *>(p.q);
+    a.k = static_cast<const uint16_t *>(p.k);
+    a.v = static_cast<const uint16_t *>(p.v);
+    a.out = static_cast<uint16_t *>(p.out);
+    a.seqlens = p.seqlens;
+    a.records = p.records;
+    a.T = p.T; a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
+    a.r = p.Hq / p.Hkv;
+    prefill_shape(a.r, &a.hpw, &a.rb);
+    a.nhc = a.r / a.hpw;
+    a.nqb = (p.T + kPRows * a.rb - 1) / (kPRows * a.rb);
+    a.scale_log2 = p.scale * kLog2e;
+    dim3 grid(a.nqb, p.Hkv * a.nhc, p.B);
+    const bool rec = p.records != nullptr;
+    if (p.d == 128)
+        return rec ? launch_p<128, true>(a, grid, stream) : launch_p<128, false>(a, grid, stream);
+    return rec ? launch_p<64, true>(a, grid, stream) : launch_p<64, false>(a, grid, stream);
 }
 
 } // namespace gqa

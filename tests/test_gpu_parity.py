@@ -126,6 +126,50 @@ def test_prefill_sweep(dtype, d):
             assert not _np(out)[1, 23:].any()
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_mfma_sweep(d):
+    # several 64-key tiles, ragged active lengths, windows crossing tile
+    # edges, and every heads-per-workgroup shape (r = 1, 2, 3, 4, 6, 8)
+    B, T, C = 3, 300, 333
+    seqlens = [300, 129, 1]
+    for hq, hkv in ((4, 4), (4, 2), (6, 2), (8, 2), (12, 2), (16, 2)):
+        assert gqa.prefill_kernel(B, T, C, hq, hkv, d) == "prefill_mfma"
+        q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, 900 + d + hq, DEV, C=C)
+        for w in (None, 1, 33, 63, 64, 65, 100):
+            out, rec = run_prefill(q, k, v, seqlens=seqlens, window=w, records=True)
+            ref, _, rrec = oracle.prefill(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
+                                          want_records=True)
+            err = _maxerr(_np(out), ref)
+            assert err <= BF16_TOL, (hq, hkv, w, err)
+            assert np.array_equal(_np(rec).astype(np.int32), rrec), (hq, hkv, w)
+
+
+def test_prefill_zero_qk_probe():
+    # equal weights: channel 2 of V holds the key index, so the output is the
+    # mean permitted key index (l + t) / 2 on every row of the MFMA kernel
+    B, T, hq, hkv, d = 2, 200, 8, 2, 128
+    q = torch.zeros((B, hq, T, d), dtype=torch.bfloat16, device=DEV)
+    k = torch.zeros((B, hkv, T, d), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros((B, hkv, T, d), dtype=torch.float32)
+    for g in range(hkv):
+        v[:, g, :, 0] = 1.0
+        v[:, g, :, 1] = float(g)
+        v[:, g, :, 2] = torch.arange(T, dtype=torch.float32)
+    v = v.to(torch.bfloat16).to(DEV)
+    for w in (None, 1, 31, 64, 65):
+        out, _ = run_prefill(q, k, v, seqlens=[200, 77], window=w)
+        o = _np(out)
+        for b, n in enumerate((200, 77)):
+            t = np.arange(T)
+            lo = np.zeros(T) if w is None else np.maximum(0, t - w + 1)
+            mean = (lo + t) / 2.0
+            act = t < n
+            assert (o[b, act, :, 0] == 1.0).all()
+            assert (o[b, act, :, 1] == (np.arange(hq) // (hq // hkv))[None, :]).all()
+            assert (np.abs(o[b, act, :, 2] - mean[act, None]) <= np.abs(mean[act, None]) * 2 ** -8).all()
+            assert not o[b, ~act].any()
+
+
 # ---------------------------------------------------------------------------
 # decode: split kernel (bf16, d in {64,128}) and generic kernel
 # ---------------------------------------------------------------------------
