@@ -18,19 +18,22 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }
 
-// Round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even (hardware v_cvt_pk_bf16_f32 on gfx950).
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// Two floats -> packed bf16 pair (low half = a).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (low half = a), one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
+
+// 2^x with the bare hardware instruction; softmax never needs results in the
+// denormal range to be accurate.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 template <typename T> struct Elem;
 template <> struct Elem<float> {

@@ -194,18 +194,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
         const float mn = fmaxf(m, tmax); // finite: key j0 is always permitted
-        const float alpha = exp2f(m - mn);
+        const float alpha = fast_exp2(m - mn);
         m = mn;
         float psum = 0.f;
-        bf16x8 pb;
+        uint32_t pw[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float p = exp2f(x[kb][i] - mn);
-                psum += p;
-                pb[kb * 4 + i] = static_cast<short>(f32_to_bf16(p));
+            for (int i = 0; i < 4; i += 2) {
+                const float p0 = fast_exp2(x[kb][i] - mn);
+                const float p1 = fast_exp2(x[kb][i + 1] - mn);
+                psum += p0 + p1;
+                pw[kb * 2 + i / 2] = pack_bf16x2(p0, p1);
             }
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
         lsum = fmaf(lsum, alpha, psum);
 #pragma unroll
         for (int i = 0; i < DB; ++i)
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w)
         mx = fmaxf(mx, sm_m[w][hl]);
-    const float my_scale = exp2f(m - mx);
+    const float my_scale = fast_exp2(m - mx);
     float *os = reinterpret_cast<float *>(smem);
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -299,7 +301,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         float hl_sum = 0.f, o = 0.f;
 #pragma unroll
         for (int w = 0; w < kDecodeWaves; ++w) {
-            hl_sum += exp2f(sm_m[w][h] - hm) * sm_l[w][h];
+            hl_sum += fast_exp2(sm_m[w][h] - hm) * sm_l[w][h];
             o += os[(w * kDecodeHeads + h) * D + c];
         }
         a.o_part[((row0 + h) * a.nsplit + split) * D + c] = o / hl_sum;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
     for (int i = 0; i < CPL; ++i)
         acc[i] = 0.f;
     for (int s = 0; s < ns; ++s) {
-        const float w = exp2f(lse[s] - mx);
+        const float w = fast_exp2(lse[s] - mx);
         den += w;
 #pragma unroll
         for (int i = 0; i < CPL; ++i)

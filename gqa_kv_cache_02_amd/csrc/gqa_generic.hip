@@ -102,8 +102,8 @@ __global__ __launch_bounds__(64) void generic_kernel(GenericArgs a) {
                 part = fmaf(qf[hh][i], kk[i], part);
             const float s = wave_sum(part) * a.scale_log2;
             const float mn = fmaxf(m[hh], s);
-            const float alpha = exp2f(m[hh] - mn);
-            const float p = exp2f(s - mn);
+            const float alpha = fast_exp2(m[hh] - mn);
+            const float p = fast_exp2(s - mn);
             l[hh] = fmaf(l[hh], alpha, p);
 #pragma unroll
             for (int i = 0; i < DPL; ++i)

@@ -42,12 +42,17 @@ struct PrefillArgs {
     const int32_t *seqlens;
     int32_t *records;
     int T, C, Hq, Hkv, window, r, hpw, rb, nhc, nqb;
-    float scale_log2;
+    float scale_log2; // |scale| * log2(e)
+    uint32_t qneg;    // 0x80008000 when scale < 0: Q's sign bits are flipped on load
 };
 
+// LDS row pitches (u16).  K rows are read 16 B per lane, 32 rows at a time:
+// a pitch of 68 dwords spreads 16 consecutive rows over all 64 banks.  V rows
+// are read with ds_read_b64_tr_b16, 4 consecutive rows per 16-lane group: a
+// pitch of 80 dwords puts those rows 16 banks apart.
 template <int D> struct PrefillSmem {
-    static constexpr int LDK = D + 8; // padded row (u16) of the K and V tiles
-    static constexpr int kTile = kPBN * LDK;
+    static constexpr int LDK = D + 8;
+    static constexpr int LDV = D + 32;
 };
 
 __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t *p) {
@@ -60,11 +65,12 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     constexpr int KS = D / 16;   // 16-feature k-steps of Q.K (32x32x16)
     constexpr int DB = D / 32;   // 32-column blocks of P.V
     constexpr int LDK = PrefillSmem<D>::LDK;
+    constexpr int LDV = PrefillSmem<D>::LDV;
     constexpr int CPR = D / 8;   // 16-byte chunks per key row
     constexpr int LPT = kPBN * CPR / 256; // 16-byte loads per thread per tensor
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[PrefillSmem<D>::kTile];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[PrefillSmem<D>::kTile];
+    __shared__ __attribute__((aligned(16))) uint16_t ks[kPBN * LDK];
+    __shared__ __attribute__((aligned(16))) uint16_t vs[kPBN * LDV];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -126,10 +132,13 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
         const uint16_t *qrow = a.q + (((int64_t)b * a.Hq + h) * a.T + (ok ? my_row : 0)) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (ok)
-                qb[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 16 + 8 * (lane >> 5));
-            else
+            if (ok) {
+                uint4 raw = *reinterpret_cast<const uint4 *>(qrow + s * 16 + 8 * (lane >> 5));
+                raw.x ^= a.qneg; raw.y ^= a.qneg; raw.z ^= a.qneg; raw.w ^= a.qneg;
+                qb[s] = __builtin_bit_cast(bf16x8, raw);
+            } else {
                 qb[s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
         }
     }
 
@@ -175,7 +184,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
             const int row = c / CPR;
             const int col = (c % CPR) * 8;
             *reinterpret_cast<uint4 *>(ks + row * LDK + col) = kreg[i];
-            *reinterpret_cast<uint4 *>(vs + row * LDK + col) = vreg[i];
+            *reinterpret_cast<uint4 *>(vs + row * LDV + col) = vreg[i];
         }
         __syncthreads();
         if (tile < tile_hi)
@@ -202,52 +211,89 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
             }
         }
 
-        // Scale, mask, running max.  Lane l holds row r0 + (l & 31) and keys
-        // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.
+        // Mask (diagonal, window-edge and padded-row tiles only) and the
+        // row's running max.  Lane l holds row r0 + (l & 31) and keys
+        // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.  Scores stay unscaled here;
+        // the scale (>= 0 after the sign flip of Q) is folded into one FMA
+        // in front of the exponential.
         const int qq = lane >> 5;
         float tmax = -INFINITY;
+        if (full) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                float x = sacc[kb][v] * a.scale_log2;
-                if (!full) {
+                for (int v = 0; v < 16; ++v)
+                    tmax = fmaxf(tmax, sacc[kb][v]);
+        } else {
+            const int lo_row = window_lo(my_row, a.window);
+            const bool row_on = my_row <= w_last;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
                     const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
-                    const bool keep = (j <= my_row) && (my_row <= w_last) &&
-                                      (j >= window_lo(my_row, a.window));
-                    x = keep ? x : -INFINITY;
+                    const bool keep = row_on && (j <= my_row) && (j >= lo_row);
+                    sacc[kb][v] = keep ? sacc[kb][v] : -INFINITY;
+                    tmax = fmaxf(tmax, sacc[kb][v]);
                 }
-                sacc[kb][v] = x;
-                tmax = fmaxf(tmax, x);
-            }
+        }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m, tmax);
-        const float msafe = (mn == -INFINITY) ? 0.f : mn;
-        const float alpha = exp2f(m - msafe);
-        m = mn;
+        tmax = (tmax == -INFINITY) ? -INFINITY : tmax * a.scale_log2;
+
+        // Lazy rescale: the reference maximum m only moves when a row's new
+        // scores exceed it by more than 2^8, so every p = 2^(x - m) stays
+        // <= 256 and the accumulators are touched only on those rare tiles.
+        // The final division by the running sum uses the same m, so the
+        // result is the same softmax.
+        const bool grow = tmax > m + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            // rows that do not grow keep m and alpha = 1 (m may still be
+            // -inf there, where m - m would be NaN)
+            const float mn = grow ? tmax : m;
+            const float alpha = grow ? fast_exp2(m - mn) : 1.f; // 0 when m was -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[i][e] *= alpha;
+            m = mn;
+        }
+        const float mneg = (m == -INFINITY) ? 0.f : -m;
         float psum = 0.f;
         bf16x8 pb[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const float p = exp2f(sacc[kb][v] - msafe);
-                psum += p;
-                pb[kb][v / 8][v % 8] = static_cast<short>(f32_to_bf16(p));
-                if (kRecord && sacc[kb][v] != -INFINITY) { // a permitted cell
-                    const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
-                    r_cnt += 1;
-                    r_xor ^= j;
-                    r_lo = min(r_lo, j);
-                    r_hi = max(r_hi, j);
+            for (int st = 0; st < 2; ++st) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int v = 8 * st + 2 * e2;
+                    float p0 = fast_exp2(fmaf(sacc[kb][v], a.scale_log2, mneg));
+                    float p1 = fast_exp2(fmaf(sacc[kb][v + 1], a.scale_log2, mneg));
+                    if (!full) { // masked cells contribute exactly 0
+                        p0 = (sacc[kb][v] == -INFINITY) ? 0.f : p0;
+                        p1 = (sacc[kb][v + 1] == -INFINITY) ? 0.f : p1;
+                    }
+                    psum += p0 + p1;
+                    w[e2] = pack_bf16x2(p0, p1);
+                    if (kRecord) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            if (sacc[kb][v + u] != -INFINITY) { // a permitted cell
+                                const int j = j0 + kb * 32 + 8 * ((v + u) / 4) + 4 * qq + ((v + u) % 4);
+                                r_cnt += 1;
+                                r_xor ^= j;
+                                r_lo = min(r_lo, j);
+                                r_hi = max(r_hi, j);
+                            }
+                        }
+                    }
                 }
+                pb[kb][st] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
             }
-        lsum = fmaf(lsum, alpha, psum);
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                oacc[i][e] *= alpha;
+        lsum += psum;
 
         // O^T += V^T . P^T.  For key block kb and k-step st, P^T k-slot
         // 8*(l>>5) + e is key kb*32 + 16*st + 8*(e/4) + 4*(l>>5) + e%4, so V^T
@@ -264,8 +310,8 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int db = 0; db < DB; ++db) {
                     const int c0 = db * 32 + 16 * cgrp + 4 * (gl & 3);
-                    const s16x4 lo4 = ds_read_tr(vs + (k0 + (gl >> 2)) * LDK + c0);
-                    const s16x4 hi4 = ds_read_tr(vs + (k0 + 8 + (gl >> 2)) * LDK + c0);
+                    const s16x4 lo4 = ds_read_tr(vs + (k0 + (gl >> 2)) * LDV + c0);
+                    const s16x4 hi4 = ds_read_tr(vs + (k0 + 8 + (gl >> 2)) * LDV + c0);
                     const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
                     oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][st], oacc[db], 0, 0, 0);
                 }
@@ -347,7 +393,8 @@ hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream) {
     prefill_shape(a.r, &a.hpw, &a.rb);
     a.nhc = a.r / a.hpw;
     a.nqb = (p.T + kPRows * a.rb - 1) / (kPRows * a.rb);
-    a.scale_log2 = p.scale * kLog2e;
+    a.scale_log2 = fabsf(p.scale) * kLog2e;
+    a.qneg = p.scale < 0.f ? 0x80008000u : 0u;
     dim3 grid(a.nqb, p.Hkv * a.nhc, p.B);
     const bool rec = p.records != nullptr;
     if (p.d == 128)
