@@ -206,7 +206,8 @@ def decode(q, k, v, *, seqlens=None, window=None, scale=None, out=None, workspac
     """Single-token decode.  q [B,Hq,d], k/v [B,Hkv,C,d] -> out [B,Hq,d].
 
     ``workspace`` is an optional uint8 device tensor of at least
-    ``decode_workspace_bytes(...)`` bytes; one is allocated when omitted."""
+    ``decode_workspace_bytes(...)`` bytes (any contents); one is allocated
+    when omitted."""
     L = _load()
     if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q must be 3-D and k, v 4-D")

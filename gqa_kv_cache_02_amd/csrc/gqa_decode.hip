@@ -13,19 +13,26 @@
 // attention (GQA)?", Step 4: the cache stores G heads and is repeated on
 // read; here the repeat never materialises).
 //
-// Inside a workgroup, 4 wavefronts take interleaved 32-key tiles.  Per tile:
+// Inside a workgroup, 4 wavefronts take interleaved 32-key tiles; each
+// wavefront prefetches its next tile while it computes the current one.
+// Per tile:
 //   S^T[32 keys x 16 heads] = K_tile[32 x d] . Q^T[d x 16]   (MFMA 16x16x32 bf16)
 //   online softmax per head in base 2 (running max m, running sum l)
 //   O^T[d x 16] += V_tile^T[d x 32] . P^T[32 x 16]            (MFMA 16x16x32 bf16)
 // The transposed products keep every per-head quantity in the lanes that own
 // that head (lane & 15), so the softmax rescale never crosses lanes.  K is
-// read straight from HBM into the MFMA operand layout; V is staged through a
-// wavefront-private LDS tile to be read back transposed.  The 4 wavefronts'
-// states are merged through LDS and one (normalised partial, log2-sum-exp)
-// pair per (row, split) goes to the workspace.  A second kernel merges the
-// splits of each row with weights 2^(lse_s - max lse) ("GQA, FlashAttention
-// and the KV cache", section "FlashAttention": blockwise softmax with a
-// numerically stable running normalisation gives the dense result).
+// read straight from HBM into the MFMA operand layout; V goes through a
+// wavefront-private LDS tile and comes back transposed (ds_read_b64_tr_b16).
+// K/V are streamed with non-temporal loads: each cell is used once.
+//
+// The 4 wavefronts' states are merged through LDS.  A row with a single chunk
+// is finished right there.  Otherwise each workgroup writes its normalised
+// partial and log2-sum-exp to the workspace, and a second, small kernel
+// merges the chunks of every row with weights 2^(lse_s - max lse) ("GQA,
+// FlashAttention and the KV cache", section "FlashAttention": blockwise
+// softmax with a numerically stable running normalisation gives the dense
+// result).  The kernel boundary orders the two steps; no workgroup waits on
+// another.
 #include <limits.h>
 
 #include "gqa_common.hpp"
@@ -33,43 +40,46 @@
 
 namespace gqa {
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 struct DecodeArgs {
     const uint16_t *q;
     const uint16_t *k;
     const uint16_t *v;
     const int32_t *seqlens;
-    float *o_part;     // [B, Hq, nsplit, D]
-    float *lse_part;   // [B, Hq, nsplit]
-    int32_t *rec_part; // [B, Hq, nsplit, 4]  (record instantiation only)
+    uint16_t *out;      // [B, Hq, D]
+    int32_t *records;   // [B, Hq, 5] (record instantiation only)
+    float *o_part;      // [B, Hq, nsplit, D]
+    float *lse_part;    // [B, Hq, nsplit]
+    int32_t *rec_part;  // [B, Hq, nsplit, 4] (record instantiation only)
     int C, Hq, Hkv, window, r, nhc, nsplit, chunk;
     float scale_log2;
 };
 
-struct CombineArgs {
-    const float *o_part;
-    const float *lse_part;
-    const int32_t *rec_part;
-    const int32_t *seqlens;
-    uint16_t *out;     // [B, Hq, D]
-    int32_t *records;  // [B, Hq, 5]
-    int B, C, Hq, r, window, nsplit, chunk;
-};
-
 template <int D> struct DecodeSmem {
-    static constexpr int LDV = D + 8; // padded LDS row (u16) of a V tile
+    // V tile pitch (u16): 72 dwords puts the 8 rows one half-wavefront reads
+    // with ds_read_b64_tr_b16 on disjoint banks.
+    static constexpr int LDV = D + 16;
     static constexpr int kVBytes = kDecodeWaves * kDecodeTile * LDV * 2;
     static constexpr int kOBytes = kDecodeWaves * kDecodeHeads * D * 4;
     static constexpr int kBytes = (kVBytes > kOBytes ? kVBytes : kOBytes);
 };
 
+__device__ __forceinline__ s16x4 ds_read_tr_d(const uint16_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4 *)(p));
+}
+
 template <int D, bool kRecord>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;               // 32-feature k-steps of Q.K
     constexpr int DB = D / 16;               // 16-column blocks of P.V
     constexpr int LDV = DecodeSmem<D>::LDV;
     constexpr int VPI = 1024 / (2 * D);      // keys per 1 KiB wavefront load
     constexpr int LPK = 64 / VPI;            // lanes per key row
     constexpr int VIT = kDecodeTile / VPI;   // V loads per tile
+    constexpr int STEP = kDecodeWaves * kDecodeTile;
 
     __shared__ __attribute__((aligned(16))) unsigned char smem[DecodeSmem<D>::kBytes];
     __shared__ float sm_m[kDecodeWaves][kDecodeHeads];
@@ -88,21 +98,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int split = blockIdx.x;
     const int h0 = g * a.r + hc * kDecodeHeads;
     const int nh = min(kDecodeHeads, a.r - hc * kDecodeHeads);
+    const int64_t row0 = (int64_t)b * a.Hq + h0; // first (b, h) row of this workgroup
 
     const int nb = a.seqlens ? a.seqlens[b] : a.C;
-    if (nb <= 0)
+    if (nb <= 0) {
+        // empty row: no key is permitted, the output row is zero
+        if (split == 0) {
+            for (int idx = tid; idx < nh * D; idx += 256)
+                a.out[row0 * D + idx] = 0;
+            if (kRecord && tid < nh) {
+                int32_t *rec = a.records + (row0 + tid) * 5;
+                rec[0] = g; rec[1] = -1; rec[2] = -1; rec[3] = 0; rec[4] = 0;
+            }
+        }
         return;
+    }
     const int hi = nb - 1;
     const int lo = window_lo(hi, a.window);
     const int c_lo = lo + split * a.chunk;
     if (c_lo > hi)
-        return; // this row has fewer chunks; the combine step knows
+        return; // this row has fewer chunks than the grid
     const int c_hi = min(hi, c_lo + a.chunk - 1);
+    const int ns = (hi - lo) / a.chunk + 1; // chunks of this row
 
     // Q^T operand: lane (hl, qg) holds features s*32 + qg*8 .. +8 of head hl.
     bf16x8 qb[KS];
     {
-        const uint16_t *qrow = a.q + ((int64_t)b * a.Hq + h0 + hl) * D;
+        const uint16_t *qrow = a.q + (row0 + hl) * D;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
             if (hl < nh)
@@ -117,6 +139,36 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const uint16_t *vbase = a.v + lane_off;
     uint16_t *vs = reinterpret_cast<uint16_t *>(smem) + wave * kDecodeTile * LDV;
 
+    // One tile's loads: K in the MFMA operand layout (lane (hl, qg) of key
+    // block kb holds key j0 + kb*16 + hl, features s*32 + qg*8 .. +8) and V in
+    // its natural layout (16 B per lane, 1 KiB per load).  Cells past the
+    // chunk end are zero-filled and never read.
+    auto load_tile = [&](int j0, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VIT]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            const int key = j0 + kb * 16 + hl;
+            const uint16_t *krow = kbase + (int64_t)key * D + qg * 8;
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                if (key <= c_hi)
+                    ka[kb][s] = __builtin_nontemporal_load(
+                        reinterpret_cast<const bf16x8 *>(krow + s * 32));
+                else
+                    ka[kb][s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+        }
+#pragma unroll
+        for (int it = 0; it < VIT; ++it) {
+            const int key = j0 + it * VPI + lane / LPK;
+            const int col = (lane % LPK) * 8;
+            if (key <= c_hi)
+                vr[it] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * D + col));
+            else
+                vr[it] = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+
     float m = -INFINITY;
     float lsum = 0.f;
     f32x4 oacc[DB];
@@ -125,47 +177,23 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     int r_cnt = 0, r_xor = 0, r_lo = INT_MAX, r_hi = -1;
 
-    for (int tile = wave;; tile += kDecodeWaves) {
-        const int j0 = c_lo + tile * kDecodeTile;
-        if (j0 > c_hi)
-            break;
-
-        // K operand straight from HBM: lane (hl, qg) of key block kb holds
-        // key j0 + kb*16 + hl, features s*32 + qg*8 .. +8.
-        bf16x8 ka[2][KS];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            const int key = j0 + kb * 16 + hl;
-            const uint16_t *krow = kbase + (int64_t)key * D + qg * 8;
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if (key <= c_hi)
-                    ka[kb][s] = *reinterpret_cast<const bf16x8 *>(krow + s * 32);
-                else
-                    ka[kb][s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
-        }
-        // V tile in its natural layout, 16 B per lane, 1 KiB per load.
-        uint4 vr[VIT];
-#pragma unroll
-        for (int it = 0; it < VIT; ++it) {
-            const int key = j0 + it * VPI + lane / LPK;
-            const int col = (lane % LPK) * 8;
-            if (key <= c_hi)
-                vr[it] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)key * D + col);
-            else
-                vr[it] = uint4{0u, 0u, 0u, 0u};
-        }
+    bf16x8 ka[2][KS], kn[2][KS];
+    u32x4 vr[VIT], vn[VIT];
+    int j0 = c_lo + wave * kDecodeTile;
+    load_tile(j0, ka, vr);
+    for (; j0 <= c_hi; j0 += STEP) {
+        load_tile(j0 + STEP, kn, vn); // next tile, in flight during this one
 
         // S^T = K . Q^T ; lane (hl, qg) gets keys kb*16 + qg*4 + i of head hl.
         f32x4 sacc[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
             sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
                 sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kb][s], qb[s], sacc[kb], 0, 0, 0);
-        }
 
         // Stage V (wavefront-private tile).  The fences keep the compiler
         // from moving LDS accesses across tiles; LDS operations of one
@@ -177,7 +205,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         for (int it = 0; it < VIT; ++it) {
             const int row = it * VPI + lane / LPK;
             const int col = (lane % LPK) * 8;
-            *reinterpret_cast<uint4 *>(vs + row * LDV + col) = vr[it];
+            *reinterpret_cast<u32x4 *>(vs + row * LDV + col) = vr[it];
         }
 
         // Scale, mask cells past the chunk end, online softmax update.
@@ -233,19 +261,27 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
         // O^T += V^T . P^T.  P^T k-slot qg*8 + e is key qg*4 + e (e < 4) or
-        // 16 + qg*4 + (e - 4): exactly the keys this lane already holds, so
-        // V^T is gathered from LDS in the same key order.
+        // 16 + qg*4 + (e - 4): exactly the keys this lane already holds.  A
+        // transposing read gives lane hl of group qg the 4 consecutive keys
+        // k0..k0+3 of column c0 + hl when lane j supplies row k0 + j/4,
+        // columns c0 + 4*(j%4) .. +3.
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-            bf16x8 va;
-            const uint16_t *vcol = vs + db * 16 + hl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int key = (e < 4) ? (qg * 4 + e) : (16 + qg * 4 + (e - 4));
-                va[e] = static_cast<short>(vcol[key * LDV]);
-            }
+            const uint16_t *src = vs + (qg * 4 + (hl >> 2)) * LDV + db * 16 + 4 * (hl & 3);
+            const s16x4 lo4 = ds_read_tr_d(src);
+            const s16x4 hi4 = ds_read_tr_d(src + 16 * LDV);
+            const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[db], 0, 0, 0);
         }
+
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                ka[kb][s] = kn[kb][s];
+#pragma unroll
+        for (int it = 0; it < VIT; ++it)
+            vr[it] = vn[it];
     }
 
     // Per-head running sum: add the 4 lane groups that share head hl.
@@ -288,7 +324,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             os[(wave * kDecodeHeads + hl) * D + db * 16 + qg * 4 + i] = oacc[db][i] * my_scale;
     __syncthreads();
 
-    const int64_t row0 = (int64_t)b * a.Hq + h0;
+    int rec_cnt = 0, rec_lo = INT_MAX, rec_hi = -1, rec_xor = 0;
+    if (kRecord) {
+#pragma unroll
+        for (int w = 0; w < kDecodeWaves; ++w) {
+            rec_cnt += sm_rec[w][0];
+            rec_lo = min(rec_lo, sm_rec[w][1]);
+            rec_hi = max(rec_hi, sm_rec[w][2]);
+            rec_xor ^= sm_rec[w][3];
+        }
+    }
+
     for (int idx = tid; idx < kDecodeHeads * D; idx += 256) {
         const int h = idx / D;
         const int c = idx % D;
@@ -304,77 +350,78 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
             hl_sum += fast_exp2(sm_m[w][h] - hm) * sm_l[w][h];
             o += os[(w * kDecodeHeads + h) * D + c];
         }
-        a.o_part[((row0 + h) * a.nsplit + split) * D + c] = o / hl_sum;
-        if (c == 0)
-            a.lse_part[(row0 + h) * a.nsplit + split] = hm + log2f(hl_sum);
+        if (ns == 1) {
+            // the whole row was this chunk: finished
+            a.out[(row0 + h) * D + c] = f32_to_bf16(o / hl_sum);
+        } else {
+            a.o_part[((row0 + h) * a.nsplit + split) * D + c] = o / hl_sum;
+            if (c == 0)
+                a.lse_part[(row0 + h) * a.nsplit + split] = hm + __builtin_amdgcn_logf(hl_sum);
+        }
     }
     if (kRecord && tid < nh) {
-        int cnt = 0, x = 0, rl = INT_MAX, rh = -1;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) {
-            cnt += sm_rec[w][0];
-            rl = min(rl, sm_rec[w][1]);
-            rh = max(rh, sm_rec[w][2]);
-            x ^= sm_rec[w][3];
+        if (ns == 1) {
+            int32_t *rec = a.records + (row0 + tid) * 5;
+            rec[0] = g; rec[1] = rec_lo; rec[2] = rec_hi; rec[3] = rec_cnt; rec[4] = rec_xor;
+        } else {
+            int32_t *rp = a.rec_part + ((row0 + tid) * a.nsplit + split) * 4;
+            rp[0] = rec_cnt; rp[1] = rec_lo; rp[2] = rec_hi; rp[3] = rec_xor;
         }
-        int32_t *rp = a.rec_part + ((row0 + tid) * a.nsplit + split) * 4;
-        rp[0] = cnt; rp[1] = rl; rp[2] = rh; rp[3] = x;
     }
 }
 
-// One wavefront per (b, h): weights 2^(lse_s - max_s lse_s) over the row's
-// splits, output = sum_s w_s o_s / sum_s w_s, rounded to bf16.
+struct MergeArgs {
+    const float *o_part;
+    const float *lse_part;
+    const int32_t *rec_part;
+    const int32_t *seqlens;
+    uint16_t *out;
+    int32_t *records;
+    int B, C, Hq, r, window, nsplit, chunk;
+};
+
+// One thread per 4 output features of a row (b, h) with more than one chunk:
+// out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max_s lse_s).
 template <int D, bool kRecord>
-__global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
-    constexpr int CPL = D / 64; // output features per lane
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
-    if (row >= (int64_t)a.B * a.Hq)
+__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+    constexpr int Q4 = D / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (int64_t)a.B * a.Hq * Q4)
         return;
+    const int64_t row = idx / Q4;
+    const int c4 = static_cast<int>(idx % Q4) * 4;
     const int b = static_cast<int>(row / a.Hq);
-    const int h = static_cast<int>(row % a.Hq);
     const int nb = a.seqlens ? a.seqlens[b] : a.C;
-    uint16_t *orow = a.out + row * D;
-    if (nb <= 0) {
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            orow[lane + 64 * i] = 0;
-        if (kRecord && lane == 0) {
-            int32_t *rec = a.records + row * 5;
-            rec[0] = h / a.r; rec[1] = -1; rec[2] = -1; rec[3] = 0; rec[4] = 0;
-        }
-        return;
-    }
+    if (nb <= 0)
+        return; // written by the split kernel
     const int hi = nb - 1;
     const int lo = window_lo(hi, a.window);
     const int ns = (hi - lo) / a.chunk + 1;
+    if (ns == 1)
+        return; // finished by the split kernel
     const float *lse = a.lse_part + row * a.nsplit;
-    const float *op = a.o_part + row * a.nsplit * D;
-
+    const float *op = a.o_part + row * a.nsplit * D + c4;
     float mx = -INFINITY;
-    for (int s = lane; s < ns; s += 64)
+    for (int s = 0; s < ns; ++s)
         mx = fmaxf(mx, lse[s]);
-    mx = wave_max(mx);
-
     float den = 0.f;
-    float acc[CPL];
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-        acc[i] = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
     for (int s = 0; s < ns; ++s) {
         const float w = fast_exp2(lse[s] - mx);
+        const float4 o = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
         den += w;
-#pragma unroll
-        for (int i = 0; i < CPL; ++i)
-            acc[i] = fmaf(w, op[(int64_t)s * D + lane + 64 * i], acc[i]);
+        acc.x = fmaf(w, o.x, acc.x);
+        acc.y = fmaf(w, o.y, acc.y);
+        acc.z = fmaf(w, o.z, acc.z);
+        acc.w = fmaf(w, o.w, acc.w);
     }
     const float inv = 1.f / den;
-#pragma unroll
-    for (int i = 0; i < CPL; ++i)
-        orow[lane + 64 * i] = f32_to_bf16(acc[i] * inv);
-
-    if (kRecord && lane == 0) {
+    uint2 pk;
+    pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+    pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    *reinterpret_cast<uint2 *>(a.out + row * D + c4) = pk;
+    if (kRecord && c4 == 0) {
         int cnt = 0, x = 0, rl = INT_MAX, rh = -1;
         for (int s = 0; s < ns; ++s) {
             const int32_t *rp = a.rec_part + (row * a.nsplit + s) * 4;
@@ -384,7 +431,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineArgs a) {
             x ^= rp[3];
         }
         int32_t *rec = a.records + row * 5;
-        rec[0] = h / a.r; rec[1] = rl; rec[2] = rh; rec[3] = cnt; rec[4] = x;
+        rec[0] = static_cast<int>(row % a.Hq) / a.r;
+        rec[1] = rl; rec[2] = rh; rec[3] = cnt; rec[4] = x;
     }
 }
 
@@ -413,11 +461,9 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window) {
     p.nsplit = elig > 0 ? (elig + p.chunk - 1) / p.chunk : 0;
     const size_t rows = (size_t)B * Hq * (size_t)p.nsplit;
     p.o_off = 0;
-    p.lse_off = align256(rows * d * sizeof(float));
+    p.lse_off = p.o_off + align256(rows * d * sizeof(float));
     p.rec_off = p.lse_off + align256(rows * sizeof(float));
     p.bytes = p.rec_off + align256(rows * 4 * sizeof(int32_t));
-    if (p.nsplit == 0)
-        p.bytes = 256; // the combine step still runs (it writes zero rows)
     return p;
 }
 
@@ -429,28 +475,27 @@ static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, h
     a.k = static_cast<const uint16_t *>(p.k);
     a.v = static_cast<const uint16_t *>(p.v);
     a.seqlens = p.seqlens;
+    a.out = static_cast<uint16_t *>(p.out);
+    a.records = p.records;
     a.o_part = reinterpret_cast<float *>(w + plan.o_off);
     a.lse_part = reinterpret_cast<float *>(w + plan.lse_off);
     a.rec_part = reinterpret_cast<int32_t *>(w + plan.rec_off);
     a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
     a.r = p.Hq / p.Hkv; a.nhc = plan.nhc; a.nsplit = plan.nsplit; a.chunk = plan.chunk;
     a.scale_log2 = p.scale * kLog2e;
-    if (plan.nsplit > 0) {
-        dim3 grid(plan.nsplit, p.Hkv * plan.nhc, p.B);
-        decode_split_kernel<D, kRecord><<<grid, 256, 0, s>>>(a);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-    }
-    CombineArgs c;
-    c.o_part = a.o_part; c.lse_part = a.lse_part; c.rec_part = a.rec_part;
-    c.seqlens = p.seqlens;
-    c.out = static_cast<uint16_t *>(p.out);
-    c.records = p.records;
-    c.B = p.B; c.C = p.C; c.Hq = p.Hq; c.r = a.r; c.window = p.window;
-    c.nsplit = plan.nsplit; c.chunk = plan.chunk;
-    const int64_t rows = (int64_t)p.B * p.Hq;
-    decode_combine_kernel<D, kRecord><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(c);
+    // at least one split so that empty rows still get their zero output
+    dim3 grid(plan.nsplit > 0 ? plan.nsplit : 1, p.Hkv * plan.nhc, p.B);
+    decode_kernel<D, kRecord><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || plan.nsplit <= 1)
+        return e; // every row finished inside the split kernel
+    MergeArgs m;
+    m.o_part = a.o_part; m.lse_part = a.lse_part; m.rec_part = a.rec_part;
+    m.seqlens = p.seqlens; m.out = a.out; m.records = p.records;
+    m.B = p.B; m.C = p.C; m.Hq = p.Hq; m.r = a.r; m.window = p.window;
+    m.nsplit = plan.nsplit; m.chunk = plan.chunk;
+    const int64_t threads = (int64_t)p.B * p.Hq * (D / 4);
+    decode_merge_kernel<D, kRecord><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, s>>>(m);
     return hipGetLastError();
 }
 

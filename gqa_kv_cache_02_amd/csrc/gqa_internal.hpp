@@ -26,12 +26,15 @@ struct Problem {
 // Split-K decode plan: the eligible key range of a row is cut into chunks of
 // `chunk` keys starting at the row's window start; each chunk is one
 // workgroup of 4 wavefronts, each wavefront taking 32-key tiles.
+// Workspace layout: partial outputs [B, Hq, nsplit, d] fp32, their
+// log2-sum-exp values [B, Hq, nsplit] fp32 and index-set partials
+// [B, Hq, nsplit, 4] int32 (each region 256-byte aligned).
 struct DecodePlan {
     int tiles_per_wave;
     int chunk;    // keys per workgroup = 4 * 32 * tiles_per_wave
     int nsplit;   // chunks per row at the longest eligible range
     int nhc;      // head chunks of up to 16 query heads per KV group
-    size_t o_off, lse_off, rec_off, bytes; // workspace layout
+    size_t o_off, lse_off, rec_off, bytes;
 };
 
 constexpr int kDecodeTile = 32;

@@ -72,7 +72,7 @@ typedef enum { GQA_F32 = 0, GQA_BF16 = 1 } gqa_dtype;
 typedef enum {
     GQA_KERNEL_NONE = 0,       /* nothing to launch (empty batch or no rows)      */
     GQA_KERNEL_GENERIC = 1,    /* one wavefront per row and KV group, fp32 or bf16 */
-    GQA_KERNEL_DECODE_SPLIT = 2, /* bf16 MFMA split-K decode + LSE combine          */
+    GQA_KERNEL_DECODE_SPLIT = 2, /* bf16 MFMA split-K decode + LSE merge kernel      */
     GQA_KERNEL_PREFILL_MFMA = 3  /* bf16 MFMA flash prefill                         */
 } gqa_kernel;
 
@@ -120,7 +120,8 @@ size_t gqa_decode_workspace_bytes(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
  *   (all n_b cells without a window).
  *   workspace: device scratch of at least gqa_decode_workspace_bytes(...)
  *   bytes, 256-byte aligned (may be NULL when that size is 0).  Its contents
- *   on entry do not matter; concurrent calls must not share one workspace.
+ *   on entry do not matter.  Calls that may overlap in time must not share
+ *   one workspace.
  *   B == 0 is a no-op returning GQA_OK.
  */
 int gqa_decode(const void *q, const void *k_cache, const void *v_cache, void *out,

@@ -249,10 +249,11 @@ def test_zero_qk_probe_index_sets():
 
 
 def test_dirty_workspace_and_side_stream():
+    # the workspace may hold anything on entry (here NaN bit patterns)
     B, C, hq, hkv, d = 4, 1000, 16, 4, 128
     q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 5, DEV)
     need = gqa.decode_workspace_bytes(B, C, hq, hkv, d)
-    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)  # NaN patterns everywhere
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device=DEV)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
         out = gqa.decode(q, k, v, seqlens=torch.tensor([1000, 999, 3, 500], dtype=torch.int32,
@@ -260,6 +261,25 @@ def test_dirty_workspace_and_side_stream():
     s.synchronize()
     ref, _, _ = oracle.decode(_np(q), _np(k), _np(v), seqlens=[1000, 999, 3, 500])
     assert _maxerr(_np(out), ref) <= BF16_TOL
+
+
+def test_workspace_reused_across_calls():
+    # one workspace for many calls with different lengths and windows
+    B, C, hq, hkv, d = 6, 3000, 8, 2, 64
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 55, DEV)
+    need = max(gqa.decode_workspace_bytes(B, C, hq, hkv, d, window=w) for w in (None, 64, 700))
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    rng = np.random.default_rng(3)
+    for i in range(12):
+        seqlens = rng.integers(0, C + 1, size=B).tolist()
+        w = (None, 64, 700)[i % 3]
+        out, rec = run_decode(q, k, v, seqlens=seqlens, window=w, records=(i % 2 == 0),
+                              workspace=ws)
+        ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
+                                     want_records=True)
+        assert _maxerr(_np(out), ref) <= BF16_TOL, (i, seqlens, w)
+        if rec is not None:
+            assert np.array_equal(_np(rec).astype(np.int32), rrec), (i, seqlens, w)
 
 
 def test_refused_call_leaves_output_untouched():
