@@ -17,8 +17,9 @@
 //   mask (diagonal, window edge and padded rows only), base-2 online softmax
 //   O^T[d x 32] += V^T[d x 64] . P^T[64 x 32]            (MFMA 32x32x16 bf16)
 // The transposed products keep every row's running max and sum in the two
-// lanes that own the row (l and l ^ 32).  V^T comes straight out of the
-// natural-layout LDS tile with ds_read_b64_tr_b16.  Tiles entirely above the
+// lanes that own the row (l and l ^ 32).  K/V tiles are double-buffered in
+// LDS and filled by direct global-to-LDS loads one tile ahead; V^T comes
+// straight out of the natural-layout LDS tile with ds_read_b64_tr_b16.  Tiles entirely above the
 // causal diagonal or entirely before every row's window start are never
 // visited; only diagonal and window-edge tiles are masked ("Intersect the
 // window with the context already permitted").
@@ -50,27 +51,42 @@ struct PrefillArgs {
 // a pitch of 68 dwords spreads 16 consecutive rows over all 64 banks.  V rows
 // are read with ds_read_b64_tr_b16, 4 consecutive rows per 16-lane group: a
 // pitch of 80 dwords puts those rows 16 banks apart.
-template <int D> struct PrefillSmem {
-    static constexpr int LDK = D + 8;
-    static constexpr int LDV = D + 32;
-};
-
 __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4 *)(p));
 }
 
+// LDS tiles are unpadded (64 rows x d bf16 each) and filled by direct
+// global-to-LDS loads, which place lane i's 16 bytes at base + 16*i.  The
+// bank spread comes from XOR-swizzling the 16-byte chunks of each row instead
+// of padding: chunk c of row r lives in slot c ^ f(r).
+//   K rows are read 16 B per lane, 16 consecutive rows per pass:
+//     f_K(r) = (r / RPL) % CPR puts those 16 reads on 16 distinct bank groups.
+//   V rows are read with ds_read_b64_tr_b16, 4 consecutive rows x 4 chunks
+//   per half-wavefront: f_V(r) = ((r / RPL) % (4 / RPL)) * 4 does the same.
+// (CPR = d/8 chunks per row, RPL = 16/CPR rows per 256-byte bank line.)
+template <int D> struct PrefillLayout {
+    static constexpr int CPR = D / 8;
+    static constexpr int RPL = 16 / CPR;
+    static constexpr int kTileBytes = kPBN * D * 2;
+    __device__ static int fk(int r) { return (r / RPL) % CPR; }
+    __device__ static int fv(int r) { return ((r / RPL) % (4 / RPL)) * 4; }
+};
+
 template <int D, bool kRecord>
-__global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void prefill_mfma_kernel(PrefillArgs a) {
+    using L = PrefillLayout<D>;
     constexpr int KS = D / 16;   // 16-feature k-steps of Q.K (32x32x16)
     constexpr int DB = D / 32;   // 32-column blocks of P.V
-    constexpr int LDK = PrefillSmem<D>::LDK;
-    constexpr int LDV = PrefillSmem<D>::LDV;
-    constexpr int CPR = D / 8;   // 16-byte chunks per key row
-    constexpr int LPT = kPBN * CPR / 256; // 16-byte loads per thread per tensor
+    constexpr int CPR = L::CPR;
+    constexpr int NLD = CPR / 4; // 1 KiB direct loads per wavefront per tensor per tile
 
-    __shared__ __attribute__((aligned(16))) uint16_t ks[kPBN * LDK];
-    __shared__ __attribute__((aligned(16))) uint16_t vs[kPBN * LDV];
+    // Two stages of [K | V] tiles.  Separate objects (and a loop unrolled by
+    // two) let the compiler see that reads of one stage never alias the
+    // direct loads in flight into the other.
+    __shared__ __attribute__((aligned(1024))) unsigned char stage0[2 * L::kTileBytes];
+    __shared__ __attribute__((aligned(1024))) unsigned char stage1[2 * L::kTileBytes];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -125,7 +141,7 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     const int w_lo_last = window_lo(r0 + kPRows - 1, a.window);
 
     // Q^T operand, kept for the whole loop: lane l holds row r0 + (l & 31),
-    // features s*16 + 8*(l >> 5) .. +8.
+    // features s*16 + 8*(l >> 5) .. +8 (sign bits flipped for a negative scale).
     bf16x8 qb[KS];
     {
         const bool ok = wave_on && my_row < a.T;
@@ -146,176 +162,202 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     const uint16_t *kbase = a.k + kv_off;
     const uint16_t *vbase = a.v + kv_off;
 
+    // Direct loads of one tile into stage st: wavefront w issues loads
+    // ii = it*4 + w; lane l fills linear chunk L = ii*64 + l, i.e. row
+    // L / CPR, slot L % CPR, with the global chunk the swizzle puts there.
+    // Rows past the workgroup's last key repeat that key (finite, masked).
+    auto load_tile = [&](int tile, unsigned char *dst) {
+        unsigned char *kst = dst;
+        unsigned char *vst = dst + L::kTileBytes;
+        const int j0 = tile * kPBN;
+#pragma unroll
+        for (int it = 0; it < NLD; ++it) {
+            const int ii = it * 4 + wave;
+            const int lin = ii * 64 + lane;
+            const int row = lin / CPR;
+            const int slot = lin % CPR;
+            const int key = min(j0 + row, wg_last);
+            const uint16_t *ksrc = kbase + (int64_t)key * D + (slot ^ L::fk(row)) * 8;
+            const uint16_t *vsrc = vbase + (int64_t)key * D + (slot ^ L::fv(row)) * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)ksrc,
+                (__attribute__((address_space(3))) void *)(kst + ii * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(
+                (const __attribute__((address_space(1))) void *)vsrc,
+                (__attribute__((address_space(3))) void *)(vst + ii * 1024), 16, 0, 0);
+        }
+    };
+
     f32x16 oacc[DB];
 #pragma unroll
     for (int i = 0; i < DB; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
             oacc[i][e] = 0.f;
-    float m = -INFINITY; // running max of this lane's row (base-2 scaled)
+    float m = -INFINITY; // reference max of this lane's row (base-2 scaled)
     float lsum = 0.f;    // this lane's share of the running sum
     int r_cnt = 0, r_xor = 0, r_lo = INT_MAX, r_hi = -1;
+    const int qq = lane >> 5;
+    const int gl = lane & 15;
+    const int cgrp = (lane >> 4) & 1; // which 16 columns of a 32-column block
 
-    // Register staging of one K/V tile: thread loads chunk c = tid + 256*i.
-    uint4 kreg[LPT], vreg[LPT];
-    auto load_tile = [&](int tile) {
-        const int j0 = tile * kPBN;
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = tid + 256 * i;
-            const int key = j0 + c / CPR;
-            const int col = (c % CPR) * 8;
-            if (key <= wg_last) {
-                kreg[i] = *reinterpret_cast<const uint4 *>(kbase + (int64_t)key * D + col);
-                vreg[i] = *reinterpret_cast<const uint4 *>(vbase + (int64_t)key * D + col);
-            } else {
-                kreg[i] = uint4{0u, 0u, 0u, 0u};
-                vreg[i] = uint4{0u, 0u, 0u, 0u};
-            }
-        }
-    };
-
-    load_tile(tile_lo);
-    for (int tile = tile_lo; tile <= tile_hi; ++tile) {
-        __syncthreads(); // every wavefront is done with the previous tile
-#pragma unroll
-        for (int i = 0; i < LPT; ++i) {
-            const int c = tid + 256 * i;
-            const int row = c / CPR;
-            const int col = (c % CPR) * 8;
-            *reinterpret_cast<uint4 *>(ks + row * LDK + col) = kreg[i];
-            *reinterpret_cast<uint4 *>(vs + row * LDV + col) = vreg[i];
-        }
-        __syncthreads();
+    // One tile: start the direct loads of the next tile into the other stage,
+    // compute on this stage, then wait until every wavefront's loads landed
+    // and every wavefront is done with this stage.
+    auto step = [&](int tile, const unsigned char *src, unsigned char *nxt) {
         if (tile < tile_hi)
-            load_tile(tile + 1); // in flight while this tile is computed
-
+            load_tile(tile + 1, nxt);
+        const unsigned char *kst = src;
+        const unsigned char *vst = src + L::kTileBytes;
         const int j0 = tile * kPBN;
-        // Skip tiles that lie wholly outside this wavefront's rows' ranges.
-        if (!wave_on || w_last < r0 || j0 > w_last || j0 + kPBN - 1 < w_lo)
-            continue;
-        const bool full = (j0 + kPBN - 1 <= r0) && (j0 >= w_lo_last) && (r0 + kPRows - 1 <= w_last);
+        const bool work = wave_on && w_last >= r0 && j0 <= w_last && j0 + kPBN - 1 >= w_lo;
+        if (work) {
+            const bool full = (j0 + kPBN - 1 <= r0) && (j0 >= w_lo_last) && (r0 + kPRows - 1 <= w_last);
 
-        // S^T = K . Q^T for two 32-key blocks.
-        f32x16 sacc[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e)
-                sacc[kb][e] = 0.f;
-            const uint16_t *krow = ks + (kb * 32 + (lane & 31)) * LDK + 8 * (lane >> 5);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(krow + s * 16);
-                sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[kb], 0, 0, 0);
-            }
-        }
-
-        // Mask (diagonal, window-edge and padded-row tiles only) and the
-        // row's running max.  Lane l holds row r0 + (l & 31) and keys
-        // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.  Scores stay unscaled here;
-        // the scale (>= 0 after the sign flip of Q) is folded into one FMA
-        // in front of the exponential.
-        const int qq = lane >> 5;
-        float tmax = -INFINITY;
-        if (full) {
+            // S^T = K . Q^T for two 32-key blocks, chains interleaved.
+            f32x16 sacc[2];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    tmax = fmaxf(tmax, sacc[kb][v]);
-        } else {
-            const int lo_row = window_lo(my_row, a.window);
-            const bool row_on = my_row <= w_last;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
-                    const bool keep = row_on && (j <= my_row) && (j >= lo_row);
-                    sacc[kb][v] = keep ? sacc[kb][v] : -INFINITY;
-                    tmax = fmaxf(tmax, sacc[kb][v]);
-                }
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        tmax = (tmax == -INFINITY) ? -INFINITY : tmax * a.scale_log2;
-
-        // Lazy rescale: the reference maximum m only moves when a row's new
-        // scores exceed it by more than 2^8, so every p = 2^(x - m) stays
-        // <= 256 and the accumulators are touched only on those rare tiles.
-        // The final division by the running sum uses the same m, so the
-        // result is the same softmax.
-        const bool grow = tmax > m + 8.f;
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-            // rows that do not grow keep m and alpha = 1 (m may still be
-            // -inf there, where m - m would be NaN)
-            const float mn = grow ? tmax : m;
-            const float alpha = grow ? fast_exp2(m - mn) : 1.f; // 0 when m was -inf
-            lsum *= alpha;
-#pragma unroll
-            for (int i = 0; i < DB; ++i)
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
-                    oacc[i][e] *= alpha;
-            m = mn;
-        }
-        const float mneg = (m == -INFINITY) ? 0.f : -m;
-        float psum = 0.f;
-        bf16x8 pb[2][2];
+                    sacc[kb][e] = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                uint32_t w[4];
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int row = kb * 32 + (lane & 31);
+                    const int c = 2 * s + qq;
+                    const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
+                        kst + (row * CPR + (c ^ L::fk(row))) * 16);
+                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[kb], 0, 0, 0);
+                }
+
+            // Mask (diagonal, window-edge and padded-row tiles only) and the
+            // row's max.  Lane l holds row r0 + (l & 31) and keys
+            // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.  Scores stay unscaled;
+            // the scale (>= 0 after the sign flip of Q) is folded into one FMA
+            // in front of the exponential.
+            float tmax = -INFINITY;
+            if (full) {
 #pragma unroll
-                for (int e2 = 0; e2 < 4; ++e2) {
-                    const int v = 8 * st + 2 * e2;
-                    float p0 = fast_exp2(fmaf(sacc[kb][v], a.scale_log2, mneg));
-                    float p1 = fast_exp2(fmaf(sacc[kb][v + 1], a.scale_log2, mneg));
-                    if (!full) { // masked cells contribute exactly 0
-                        p0 = (sacc[kb][v] == -INFINITY) ? 0.f : p0;
-                        p1 = (sacc[kb][v + 1] == -INFINITY) ? 0.f : p1;
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        tmax = fmaxf(tmax, sacc[kb][v]);
+            } else {
+                const int lo_row = window_lo(my_row, a.window);
+                const bool row_on = my_row <= w_last;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
+                        const bool keep = row_on && (j <= my_row) && (j >= lo_row);
+                        sacc[kb][v] = keep ? sacc[kb][v] : -INFINITY;
+                        tmax = fmaxf(tmax, sacc[kb][v]);
                     }
-                    psum += p0 + p1;
-                    w[e2] = pack_bf16x2(p0, p1);
-                    if (kRecord) {
+            }
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                                 __float_as_uint(tmax), false, false);
+                tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])); // lanes l and l^32
+            }
+            tmax = (tmax == -INFINITY) ? -INFINITY : tmax * a.scale_log2;
+
+            // Lazy rescale: the reference maximum m only moves when a row's new
+            // scores exceed it by more than 2^8, so every p = 2^(x - m) stays
+            // <= 256 and the accumulators are touched only on those rare
+            // tiles.  The final division by the running sum uses the same m,
+            // so the result is the same softmax.
+            const bool grow = tmax > m + 8.f;
+            if (__builtin_amdgcn_ballot_w64(grow)) {
+                // rows that do not grow keep m and alpha = 1 (m may still be
+                // -inf there, where m - m would be NaN)
+                const float mn = grow ? tmax : m;
+                const float alpha = grow ? fast_exp2(m - mn) : 1.f; // 0 when m was -inf
+                lsum *= alpha;
 #pragma unroll
-                        for (int u = 0; u < 2; ++u) {
-                            if (sacc[kb][v + u] != -INFINITY) { // a permitted cell
-                                const int j = j0 + kb * 32 + 8 * ((v + u) / 4) + 4 * qq + ((v + u) % 4);
-                                r_cnt += 1;
-                                r_xor ^= j;
-                                r_lo = min(r_lo, j);
-                                r_hi = max(r_hi, j);
+                for (int i = 0; i < DB; ++i)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        oacc[i][e] *= alpha;
+                m = mn;
+            }
+            const float mneg = (m == -INFINITY) ? 0.f : -m;
+            float psum = 0.f;
+            bf16x8 pb[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int stp = 0; stp < 2; ++stp) {
+                    uint32_t w[4];
+#pragma unroll
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        const int v = 8 * stp + 2 * e2;
+                        float p0 = fast_exp2(fmaf(sacc[kb][v], a.scale_log2, mneg));
+                        float p1 = fast_exp2(fmaf(sacc[kb][v + 1], a.scale_log2, mneg));
+                        if (!full) { // masked cells contribute exactly 0
+                            p0 = (sacc[kb][v] == -INFINITY) ? 0.f : p0;
+                            p1 = (sacc[kb][v + 1] == -INFINITY) ? 0.f : p1;
+                        }
+                        psum += p0 + p1;
+                        w[e2] = pack_bf16x2(p0, p1);
+                        if (kRecord) {
+#pragma unroll
+                            for (int u = 0; u < 2; ++u) {
+                                if (sacc[kb][v + u] != -INFINITY) { // a permitted cell
+                                    const int j = j0 + kb * 32 + 8 * ((v + u) / 4) + 4 * qq + ((v + u) % 4);
+                                    r_cnt += 1;
+                                    r_xor ^= j;
+                                    r_lo = min(r_lo, j);
+                                    r_hi = max(r_hi, j);
+                                }
                             }
                         }
                     }
+                    pb[kb][stp] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
                 }
-                pb[kb][st] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
-            }
-        lsum += psum;
+            lsum += psum;
 
-        // O^T += V^T . P^T.  For key block kb and k-step st, P^T k-slot
-        // 8*(l>>5) + e is key kb*32 + 16*st + 8*(e/4) + 4*(l>>5) + e%4, so V^T
-        // needs two runs of 4 consecutive keys per lane: a transposing LDS read
-        // per run.  In each 16-lane group, lane j supplies row k0 + j/4,
-        // columns c0 + 4*(j%4) .. +3 and receives column c0 + (lane & 15).
-        const int gl = lane & 15;
-        const int cgrp = (lane >> 4) & 1; // which 16 columns of the 32
+            // O^T += V^T . P^T.  For key block kb and k-step stp, P^T k-slot
+            // 8*(l>>5) + e is key kb*32 + 16*stp + 8*(e/4) + 4*(l>>5) + e%4, so
+            // V^T needs two runs of 4 consecutive keys per lane: one
+            // transposing LDS read per run.  In each 16-lane group, lane j
+            // supplies row k0 + j/4, columns c0 + 4*(j%4) .. +3 and receives
+            // column c0 + (lane & 15).
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                const int k0 = kb * 32 + 16 * st + 4 * qq;
+                for (int stp = 0; stp < 2; ++stp) {
+                    const int k0 = kb * 32 + 16 * stp + 4 * qq;
 #pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const int c0 = db * 32 + 16 * cgrp + 4 * (gl & 3);
-                    const s16x4 lo4 = ds_read_tr(vs + (k0 + (gl >> 2)) * LDV + c0);
-                    const s16x4 hi4 = ds_read_tr(vs + (k0 + 8 + (gl >> 2)) * LDV + c0);
-                    const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][st], oacc[db], 0, 0, 0);
+                    for (int db = 0; db < DB; ++db) {
+                        const int col = db * 32 + 16 * cgrp + 4 * (gl & 3);
+                        const int ra = k0 + (gl >> 2);
+                        const int rb2 = ra + 8;
+                        const unsigned char *pa =
+                            vst + (ra * CPR + ((col >> 3) ^ L::fv(ra))) * 16 + (col & 7) * 2;
+                        const unsigned char *pb2 =
+                            vst + (rb2 * CPR + ((col >> 3) ^ L::fv(rb2))) * 16 + (col & 7) * 2;
+                        const s16x4 lo4 = ds_read_tr(reinterpret_cast<const uint16_t *>(pa));
+                        const s16x4 hi4 = ds_read_tr(reinterpret_cast<const uint16_t *>(pb2));
+                        const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][stp], oacc[db], 0, 0, 0);
+                    }
                 }
-            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): next tile's loads of this wavefront landed
+        __syncthreads();                     // ... of every wavefront; this stage is free again
+    };
+
+    load_tile(tile_lo, stage0);
+    __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): this wavefront's tile loads landed
+    __syncthreads();
+    for (int tile = tile_lo; tile <= tile_hi; tile += 2) {
+        step(tile, stage0, stage1);
+        if (tile + 1 > tile_hi)
+            break;
+        step(tile + 1, stage1, stage0);
     }
 
     if (!wave_on)
@@ -332,7 +374,6 @@ __global__ __launch_bounds__(256) void prefill_mfma_kernel(PrefillArgs a) {
     const bool active = my_row < nb;
     const float inv = (active && lsum > 0.f) ? 1.f / lsum : 0.f;
     uint16_t *orow = a.out + ((int64_t)b * a.T + my_row) * out_stride + (int64_t)h * D;
-    const int qq = lane >> 5;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
