@@ -51,6 +51,22 @@ struct PrefillArgs {
 // a pitch of 68 dwords spreads 16 consecutive rows over all 64 banks.  V rows
 // are read with ds_read_b64_tr_b16, 4 consecutive rows per 16-lane group: a
 // pitch of 80 dwords puts those rows 16 banks apart.
+// Direct global-to-LDS 16-byte load (lane i lands at lds_addr + 16*i).  It is
+// issued from inline assembly so that the compiler, which cannot tell which
+// LDS bytes the transfer writes, does not put a wait for it in front of every
+// transposing LDS read of the other stage.  It has no register result; the
+// kernel itself waits for it (vmcnt(0), then a workgroup barrier) before the
+// stage it fills is read.
+__device__ __forceinline__ void dma16(const uint16_t *gptr, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %1, off" : : "{m0}"(lds_addr), "v"(gptr) : "memory");
+}
+
+// Byte offset of an LDS object in the workgroup's LDS allocation.
+__device__ __forceinline__ uint32_t lds_offset(const void *p) {
+    return static_cast<uint32_t>(
+        reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+
 __device__ __forceinline__ s16x4 ds_read_tr(const uint16_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) s16x4 *)(p));
@@ -90,6 +106,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave); // same value, kept in an SGPR
     const int lane = tid & 63;
     const int nwaves = a.hpw * a.rb;
 
@@ -166,25 +183,19 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // ii = it*4 + w; lane l fills linear chunk L = ii*64 + l, i.e. row
     // L / CPR, slot L % CPR, with the global chunk the swizzle puts there.
     // Rows past the workgroup's last key repeat that key (finite, masked).
-    auto load_tile = [&](int tile, unsigned char *dst) {
-        unsigned char *kst = dst;
-        unsigned char *vst = dst + L::kTileBytes;
+    auto load_tile = [&](int tile, uint32_t dst) {
         const int j0 = tile * kPBN;
 #pragma unroll
         for (int it = 0; it < NLD; ++it) {
-            const int ii = it * 4 + wave;
+            const int ii = it * 4 + wave_u;
             const int lin = ii * 64 + lane;
             const int row = lin / CPR;
             const int slot = lin % CPR;
             const int key = min(j0 + row, wg_last);
             const uint16_t *ksrc = kbase + (int64_t)key * D + (slot ^ L::fk(row)) * 8;
             const uint16_t *vsrc = vbase + (int64_t)key * D + (slot ^ L::fv(row)) * 8;
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)ksrc,
-                (__attribute__((address_space(3))) void *)(kst + ii * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(
-                (const __attribute__((address_space(1))) void *)vsrc,
-                (__attribute__((address_space(3))) void *)(vst + ii * 1024), 16, 0, 0);
+            dma16(ksrc, dst + ii * 1024);
+            dma16(vsrc, dst + L::kTileBytes + ii * 1024);
         }
     };
 
@@ -206,7 +217,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // and every wavefront is done with this stage.
     auto step = [&](int tile, const unsigned char *src, unsigned char *nxt) {
         if (tile < tile_hi)
-            load_tile(tile + 1, nxt);
+            load_tile(tile + 1, lds_offset(nxt));
         const unsigned char *kst = src;
         const unsigned char *vst = src + L::kTileBytes;
         const int j0 = tile * kPBN;
@@ -350,7 +361,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
         __syncthreads();                     // ... of every wavefront; this stage is free again
     };
 
-    load_tile(tile_lo, stage0);
+    load_tile(tile_lo, lds_offset(stage0));
     __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): this wavefront's tile loads landed
     __syncthreads();
     for (int tile = tile_lo; tile <= tile_hi; tile += 2) {
