@@ -25,6 +25,8 @@
 // window with the context already permitted").
 #include <limits.h>
 
+#include <type_traits>
+
 #include "gqa_common.hpp"
 #include "gqa_internal.hpp"
 
@@ -222,9 +224,11 @@ void prefill_mfma_kernel(PrefillArgs a) {
         const unsigned char *vst = src + L::kTileBytes;
         const int j0 = tile * kPBN;
         const bool work = wave_on && w_last >= r0 && j0 <= w_last && j0 + kPBN - 1 >= w_lo;
-        if (work) {
-            const bool full = (j0 + kPBN - 1 <= r0) && (j0 >= w_lo_last) && (r0 + kPRows - 1 <= w_last);
-
+        // Interior tiles (every key permitted for every row of the wavefront)
+        // and edge tiles (diagonal, window edge, padded rows) are separate
+        // instantiations so that interior tiles carry no masking code.
+        auto compute = [&](auto full_tag) {
+            constexpr bool full = decltype(full_tag)::value;
             // S^T = K . Q^T for two 32-key blocks, chains interleaved.
             f32x16 sacc[2];
 #pragma unroll
@@ -249,7 +253,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
             // the scale (>= 0 after the sign flip of Q) is folded into one FMA
             // in front of the exponential.
             float tmax = -INFINITY;
-            if (full) {
+            if constexpr (full) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -307,7 +311,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         const int v = 8 * stp + 2 * e2;
                         float p0 = fast_exp2(fmaf(sacc[kb][v], a.scale_log2, mneg));
                         float p1 = fast_exp2(fmaf(sacc[kb][v + 1], a.scale_log2, mneg));
-                        if (!full) { // masked cells contribute exactly 0
+                        if constexpr (!full) { // masked cells contribute exactly 0
                             p0 = (sacc[kb][v] == -INFINITY) ? 0.f : p0;
                             p1 = (sacc[kb][v + 1] == -INFINITY) ? 0.f : p1;
                         }
@@ -356,6 +360,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
                         oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][stp], oacc[db], 0, 0, 0);
                     }
                 }
+                };
+        if (work) {
+            if ((j0 + kPBN - 1 <= r0) && (j0 >= w_lo_last) && (r0 + kPRows - 1 <= w_last))
+                compute(std::true_type{});
+            else
+                compute(std::false_type{});
         }
         __builtin_amdgcn_s_waitcnt(0x0F70); // vmcnt(0): next tile's loads of this wavefront landed
         __syncthreads();                     // ... of every wavefront; this stage is free again
