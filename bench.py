@@ -2,24 +2,34 @@
 (MFMA-bound) on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-prefill] [--copy-calibration]
 
-A step is one decode call (all query heads of every sequence against its
-cached prefix) on the headline workload: B=8, Hq=32, Hkv=8, d=128, 8000
-cached cells per sequence, bf16 storage, iid N(0,1) synthetic inputs.  The
-inputs are resident in HBM before timing starts.  Four copies of the K/V cache
-are rotated so that no step finds its cache in the 256 MB Infinity Cache left
-over from the previous step.
+A step is one decode call -- every query head of every sequence against its
+cached prefix, i.e. the split kernel and the merge kernel -- on the headline
+workload: B=8, Hq=32, Hkv=8, d=128, 8000 cached cells per sequence, bf16
+storage, iid N(0,1) synthetic inputs resident in HBM before timing starts.
+Four copies of the K/V cache are rotated so that no step finds its cache in the
+256 MB Infinity Cache left over from the previous step.
 
-Prints ONE JSON line.  `value` is algorithmic HBM GB/s (K/V cells read once
-per KV group, plus Q and O) over the timed steps; `roofline` relates the decode
-kernel's own per-launch duration (HIP events on its stream) to the 8 TB/s HBM
-peak; `prefill` reports the causal prefill (B=1, T=4096, Hq=32, Hkv=8,
-d=128) in TFLOP/s against the 2.5 PFLOP/s dense bf16 peak; `cpu_baseline`
-times the fp64 oracle on the host cores on the same decode workload.
+Prints ONE JSON line.
+  value          algorithmic HBM GB/s (K/V cells read once per KV group, plus
+                 Q read and O written) over K back-to-back timed steps.
+  roofline       the decode call's own duration (HIP events recorded on the
+                 launch stream around each call, second pass), against the
+                 8 TB/s HBM3E peak.  `traffic` is the HBM bytes per call that
+                 rocprofv3 counters measured (profiles/, scaled by a plain
+                 copy of known size), reported only while the kernel source
+                 still has the hash the counters were taken with.
+  prefill        causal prefill B=1, T=4096, Hq=32, Hkv=8, d=128: TFLOP/s of
+                 the permitted pairs (4*d flops each) against 2.5 PFLOP/s
+                 dense bf16 MFMA.
+  cpu_baseline   the fp64 oracle (plain C, OpenMP) on the host cores, on the
+                 same decode workload.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,6 +41,9 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+COPY_CAL_BYTES = 1 << 30  # plain copy used to calibrate the traffic counters
+DECODE_SRC = os.path.join(ROOT, "gqa_kv_cache_02_amd", "csrc", "gqa_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b8_hq32_hkv8_d128_n8000_traffic.txt")
 
 
 def decode_bytes(B, Hq, Hkv, d, cells, elem=2):
@@ -44,8 +57,26 @@ def prefill_flops(Hq, d, T, B=1):
     return 4 * Hq * d * B * T * (T + 1) // 2
 
 
-def _events(torch, n):
-    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for ln in open(TRAFFIC_FILE):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("decode_source_sha256_16") != source_hash(DECODE_SRC):
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
 
 
 def bench_decode(torch, gqa, synth, steps, warmup):
@@ -61,7 +92,7 @@ def bench_decode(torch, gqa, synth, steps, warmup):
         vs.append(v)
     seqlens = torch.full((B,), n, dtype=torch.int32, device=dev)
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
-    ws = torch.zeros(max(1, gqa.decode_workspace_bytes(B, C, hq, hkv, d)), dtype=torch.uint8,
+    ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, C, hq, hkv, d)), dtype=torch.uint8,
                      device=dev)
     kernel = gqa.decode_kernel(B, C, hq, hkv, d)
 
@@ -70,28 +101,29 @@ def bench_decode(torch, gqa, synth, steps, warmup):
 
     for i in range(warmup):
         step(i)
+    # timed region: K back-to-back steps, synchronised on both sides
     torch.cuda.synchronize()
-    # per-launch durations, events on the launch stream (torch's current stream)
-    ev = _events(torch, 2 * steps)
-    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    start_all = torch.cuda.Event(enable_timing=True)
-    end_all = torch.cuda.Event(enable_timing=True)
-    start_all.record()
+    start.record()
+    for i in range(steps):
+        step(i)
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(stop) / steps
+    # second pass: events on the launch stream around each call
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for i in range(steps):
         ev[2 * i].record()
         step(i)
         ev[2 * i + 1].record()
-    end_all.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    total_ms = start_all.elapsed_time(end_all)
-    per_launch = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
-    nbytes = decode_bytes(B, hq, hkv, d, n)
-    ms = total_ms / steps
-    avg_launch_ms = sum(per_launch) / steps
-    return dict(cfg=cfg, kernel=kernel, ms=ms, wall_s=wall, avg_launch_ms=avg_launch_ms,
-                min_launch_ms=min(per_launch), nbytes=nbytes, q=q, k=k0, v=v0, seqlens=[n] * B)
+    per_call = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+    return dict(cfg=cfg, kernel=kernel, ms=ms, wall_s=wall,
+                avg_call_ms=sum(per_call) / steps, min_call_ms=min(per_call),
+                nbytes=decode_bytes(B, hq, hkv, d, n), q=q, k=k0, v=v0, seqlens=[n] * B)
 
 
 def bench_prefill(torch, gqa, synth, steps, warmup):
@@ -103,7 +135,7 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
     for _ in range(warmup):
         gqa.prefill(q, k, v, out=out)
     torch.cuda.synchronize()
-    ev = _events(torch, 2 * steps)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for i in range(steps):
         ev[2 * i].record()
         gqa.prefill(q, k, v, out=out)
@@ -117,10 +149,42 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
                 kernel=gqa.prefill_kernel(B, T, T, hq, hkv, d), ms=round(ms, 5),
                 flops=flops, tflops=round(tflops, 2),
                 frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
-                tokens_per_s=round(B * T / (ms * 1e-3), 1))
+                tokens_per_s=round(B * T / (ms * 1e-3), 1),
+                timing="HIP events on the launch stream around each call")
 
 
-def cpu_baseline(torch, r, budget_s=12.0):
+def copy_calibration(torch):
+    """A plain device copy of COPY_CAL_BYTES, so that rocprofv3's FETCH_SIZE
+    and WRITE_SIZE counters can be scaled against a known transfer."""
+    src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def hbm_copy_reference(torch, nbytes=1 << 30, reps=10):
+    """Read+write GB/s of a plain 1 GiB device copy (torch copy_) on this
+    GPU: a measured practical ceiling to read the roofline fraction against."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
+
+
+def cpu_baseline(r, budget_s=12.0):
     """The fp64 oracle as it stands, on the host cores, on the decode workload."""
     import numpy as np
 
@@ -131,7 +195,7 @@ def cpu_baseline(torch, r, budget_s=12.0):
     v = r["v"].float().cpu().numpy().astype(np.float64)
     oracle.lib()
     runs, t_total = 0, 0.0
-    while t_total < budget_s and runs < 50:
+    while t_total < budget_s and runs < 400:
         t0 = time.perf_counter()
         oracle.decode(q, k, v, seqlens=r["seqlens"])
         t_total += time.perf_counter() - t0
@@ -139,22 +203,24 @@ def cpu_baseline(torch, r, budget_s=12.0):
     per = t_total / runs
     return dict(value=round(r["nbytes"] / per / 1e9, 3), unit="GB/s", cores=oracle.threads(),
                 kind="oracle",
-                sample=f"full decode workload (B=8, Hq=32, Hkv=8, d=128, 8000 cells) in fp64, "
-                       f"{runs} runs, {per:.3f} s each, inputs pre-converted to float64")
+                sample=f"the whole decode workload (B=8, Hq=32, Hkv=8, d=128, 8000 cells) in "
+                       f"fp64, {runs} runs of {per:.4f} s; inputs converted to float64 "
+                       "before timing")
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the decode and prefill paths shard over sequences or KV groups with no "
-              "exchange, so there is nothing multi-GPU to time here)", file=sys.stderr)
+              "(decode and prefill shard over sequences or KV groups with no exchange, so "
+              "there is no multi-GPU step to time)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -166,7 +232,7 @@ def main():
     r = bench_decode(torch, gqa, synth, args.steps, args.warmup)
     cfg = r["cfg"]
     gbs = r["nbytes"] / (r["ms"] * 1e-3) / 1e9
-    achieved = r["nbytes"] / (r["avg_launch_ms"] * 1e-3) / 1e9
+    achieved = r["nbytes"] / (r["avg_call_ms"] * 1e-3) / 1e9
     line = {
         "metric": "GQA decode achieved HBM GB/s & % peak; causal prefill TFLOP/s & % MFMA peak",
         "value": round(gbs, 2),
@@ -188,15 +254,21 @@ def main():
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": measured_traffic(),
                      "bytes_per_launch": r["nbytes"],
-                     "avg_launch_ms": round(r["avg_launch_ms"], 5),
-                     "timing": "HIP events around each decode call on its stream"},
+                     "avg_launch_ms": round(r["avg_call_ms"], 5),
+                     "min_launch_ms": round(r["min_call_ms"], 5),
+                     "kernel": "decode call = decode_kernel (split) + decode_merge_kernel",
+                     "timing": "HIP events on the launch stream around each decode call"},
     }
+    line["roofline"]["hbm_copy_reference_gbs"] = hbm_copy_reference(torch)
     if not args.no_prefill:
-        line["prefill"] = bench_prefill(torch, gqa, synth, max(5, args.steps // 10), 3)
+        line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3)
+    if args.copy_calibration:
+        copy_calibration(torch)
+        line["copy_calibration_bytes"] = COPY_CAL_BYTES
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(torch, r)
+        line["cpu_baseline"] = cpu_baseline(r)
     print(json.dumps(line), flush=True)
 
 
