@@ -44,7 +44,7 @@ struct PrefillArgs {
     uint16_t *out;
     const int32_t *seqlens;
     int32_t *records;
-    int T, C, Hq, Hkv, window, r, hpw, rb, nhc, nqb;
+    int B, T, C, Hq, Hkv, window, r, hpw, rb, nhc, nqb;
     float scale_log2; // |scale| * log2(e)
     uint32_t qneg;    // 0x80008000 when scale < 0: Q's sign bits are flipped on load
 };
@@ -61,6 +61,11 @@ struct PrefillArgs {
 // stage it fills is read.
 __device__ __forceinline__ void dma16(const uint16_t *gptr, uint32_t lds_addr) {
     asm volatile("global_load_lds_dwordx4 %1, off" : : "{m0}"(lds_addr), "v"(gptr) : "memory");
+}
+// Same, with a wave-uniform 64-bit base in SGPRs and a 32-bit per-lane byte
+// offset (no per-lane 64-bit address arithmetic on interior tiles).
+__device__ __forceinline__ void dma16s(const void *sbase, uint32_t voff, uint32_t lds_addr) {
+    asm volatile("global_load_lds_dwordx4 %1, %2" : : "{m0}"(lds_addr), "v"(voff), "s"(sbase) : "memory");
 }
 
 // Byte offset of an LDS object in the workgroup's LDS allocation.
@@ -112,10 +117,19 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int lane = tid & 63;
     const int nwaves = a.hpw * a.rb;
 
-    const int b = blockIdx.z;
-    const int g = blockIdx.y / a.nhc;
-    const int hc = blockIdx.y % a.nhc;
-    const int qblk = a.nqb - 1 - static_cast<int>(blockIdx.x); // heaviest blocks first
+    // One-dimensional grid, query block slowest: workgroups are dispatched
+    // in order of their linear index, so every head's heaviest (latest)
+    // causal blocks start first and the light ones fill the tail.  Adjacent
+    // indices differ in (batch row, KV group, head chunk); with 8 or a
+    // multiple of them per query block, each XCD keeps seeing the same KV
+    // groups, whose K/V then stay in that XCD's L2.
+    const int per_blk = a.B * a.Hkv * a.nhc;
+    const int lin_id = static_cast<int>(blockIdx.x);
+    const int qblk = a.nqb - 1 - lin_id / per_blk; // heaviest blocks first
+    const int rest = lin_id % per_blk;
+    const int b = rest / (a.Hkv * a.nhc);
+    const int g = (rest / a.nhc) % a.Hkv;
+    const int hc = rest % a.nhc;
     const int rows_wg = kPRows * a.rb;
     const int q0 = qblk * rows_wg;
 
@@ -161,19 +175,26 @@ void prefill_mfma_kernel(PrefillArgs a) {
 
     // Q^T operand, kept for the whole loop: lane l holds row r0 + (l & 31),
     // features s*16 + 8*(l >> 5) .. +8 (sign bits flipped for a negative scale).
+    // The loads are issued unconditionally from a valid row (row 0 of a head
+    // of this group for idle lanes) so that all of them are in flight at
+    // once; lanes without a row zero their operand afterwards.
     bf16x8 qb[KS];
     {
         const bool ok = wave_on && my_row < a.T;
-        const uint16_t *qrow = a.q + (((int64_t)b * a.Hq + h) * a.T + (ok ? my_row : 0)) * D;
+        const int hq = wave_on ? h : g * a.r;
+        const uint16_t *qrow = a.q + (((int64_t)b * a.Hq + hq) * a.T + (ok ? my_row : 0)) * D;
+        uint4 raw[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
+            raw[s] = *reinterpret_cast<const uint4 *>(qrow + s * 16 + 8 * (lane >> 5));
+        const uint32_t keep = ok ? 0xFFFFFFFFu : 0u;
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (ok) {
-                uint4 raw = *reinterpret_cast<const uint4 *>(qrow + s * 16 + 8 * (lane >> 5));
-                raw.x ^= a.qneg; raw.y ^= a.qneg; raw.z ^= a.qneg; raw.w ^= a.qneg;
-                qb[s] = __builtin_bit_cast(bf16x8, raw);
-            } else {
-                qb[s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
+            raw[s].x = (raw[s].x ^ a.qneg) & keep;
+            raw[s].y = (raw[s].y ^ a.qneg) & keep;
+            raw[s].z = (raw[s].z ^ a.qneg) & keep;
+            raw[s].w = (raw[s].w ^ a.qneg) & keep;
+            qb[s] = __builtin_bit_cast(bf16x8, raw[s]);
         }
     }
 
@@ -181,23 +202,44 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const uint16_t *kbase = a.k + kv_off;
     const uint16_t *vbase = a.v + kv_off;
 
-    // Direct loads of one tile into stage st: wavefront w issues loads
-    // ii = it*4 + w; lane l fills linear chunk L = ii*64 + l, i.e. row
-    // L / CPR, slot L % CPR, with the global chunk the swizzle puts there.
-    // Rows past the workgroup's last key repeat that key (finite, masked).
+    // Direct loads of one tile into a stage: wavefront w issues loads
+    // ii = it*4 + w; lane l fills linear chunk ii*64 + l, i.e. row
+    // (ii*64 + l) / CPR and slot (ii*64 + l) % CPR, with the global chunk the
+    // swizzle puts there.  An interior tile uses per-lane byte offsets fixed
+    // for the whole loop; the workgroup's last tile repeats its last key in
+    // the rows past it (finite data, always masked).
+    uint32_t koffs[NLD], voffs[NLD];
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+        const int ii = it * 4 + wave_u;
+        const int lin = ii * 64 + lane;
+        const int row = lin / CPR;
+        const int slot = lin % CPR;
+        koffs[it] = static_cast<uint32_t>(row * D * 2 + (slot ^ L::fk(row)) * 16);
+        voffs[it] = static_cast<uint32_t>(row * D * 2 + (slot ^ L::fv(row)) * 16);
+    }
     auto load_tile = [&](int tile, uint32_t dst) {
         const int j0 = tile * kPBN;
+        if (j0 + kPBN - 1 <= wg_last) {
+            const void *kb0 = kbase + (int64_t)j0 * D;
+            const void *vb0 = vbase + (int64_t)j0 * D;
 #pragma unroll
-        for (int it = 0; it < NLD; ++it) {
-            const int ii = it * 4 + wave_u;
-            const int lin = ii * 64 + lane;
-            const int row = lin / CPR;
-            const int slot = lin % CPR;
-            const int key = min(j0 + row, wg_last);
-            const uint16_t *ksrc = kbase + (int64_t)key * D + (slot ^ L::fk(row)) * 8;
-            const uint16_t *vsrc = vbase + (int64_t)key * D + (slot ^ L::fv(row)) * 8;
-            dma16(ksrc, dst + ii * 1024);
-            dma16(vsrc, dst + L::kTileBytes + ii * 1024);
+            for (int it = 0; it < NLD; ++it) {
+                const int ii = it * 4 + wave_u;
+                dma16s(kb0, koffs[it], dst + ii * 1024);
+                dma16s(vb0, voffs[it], dst + L::kTileBytes + ii * 1024);
+            }
+        } else {
+#pragma unroll
+            for (int it = 0; it < NLD; ++it) {
+                const int ii = it * 4 + wave_u;
+                const int lin = ii * 64 + lane;
+                const int row = lin / CPR;
+                const int slot = lin % CPR;
+                const int key = min(j0 + row, wg_last);
+                dma16(kbase + (int64_t)key * D + (slot ^ L::fk(row)) * 8, dst + ii * 1024);
+                dma16(vbase + (int64_t)key * D + (slot ^ L::fv(row)) * 8, dst + L::kTileBytes + ii * 1024);
+            }
         }
     };
 
@@ -429,11 +471,18 @@ static void prefill_shape(int r, int *hpw, int *rb) {
     *rb = (4 % best == 0) ? 4 / best : 1;
 }
 
-bool prefill_grid_ok(int B, int T, int Hq, int Hkv) {
+// The grid is one-dimensional: ceil(T / (32*rb)) * B * Hkv * (r/hpw)
+// workgroups of 256 work-items, whose total must fit a 32-bit count.
+static int64_t prefill_workgroups(int B, int T, int Hq, int Hkv) {
     int hpw, rb;
     prefill_shape(Hq / Hkv, &hpw, &rb);
-    const int64_t y = (int64_t)Hkv * ((Hq / Hkv) / hpw);
-    return B <= 65535 && y <= 65535 && T >= 0;
+    const int64_t nqb = ((int64_t)T + kPRows * rb - 1) / (kPRows * rb);
+    return nqb * B * Hkv * ((Hq / Hkv) / hpw);
+}
+
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv) {
+    const int64_t wgs = prefill_workgroups(B, T, Hq, Hkv);
+    return T >= 0 && wgs * 256 <= (int64_t)UINT32_MAX;
 }
 
 template <int D, bool kRecord>
@@ -457,7 +506,8 @@ hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream) {
     a.nqb = (p.T + kPRows * a.rb - 1) / (kPRows * a.rb);
     a.scale_log2 = fabsf(p.scale) * kLog2e;
     a.qneg = p.scale < 0.f ? 0x80008000u : 0u;
-    dim3 grid(a.nqb, p.Hkv * a.nhc, p.B);
+    a.B = p.B;
+    dim3 grid(static_cast<uint32_t>(prefill_workgroups(p.B, p.T, p.Hq, p.Hkv)), 1, 1);
     const bool rec = p.records != nullptr;
     if (p.d == 128)
         return rec ? launch_p<128, true>(a, grid, stream) : launch_p<128, false>(a, grid, stream);
