@@ -57,6 +57,12 @@ def lib():
         L.oracle_expanded.argtypes = ([dp, dp, dp, dp, ip] + [i32] * 7 + [ctypes.c_double]
                                       + [i32, i32])
         L.oracle_expanded.restype = i32
+        L.oracle_attend_prefix.argtypes = ([dp, dp, dp, dp, dp, ip, ip, ip, ip] + [i32] * 7
+                                           + [ctypes.c_double])
+        L.oracle_attend_prefix.restype = i32
+        L.oracle_decode_cache.argtypes = ([dp, dp, dp, dp, dp, dp, ip, ip] + [i32] * 6
+                                          + [ctypes.c_double, i32])
+        L.oracle_decode_cache.restype = i32
         _lib = L
     return _lib
 
@@ -172,3 +178,57 @@ def expanded(q, k, v, seqlens=None, window=None, scale=None, decode=False, tiled
     if rc:
         raise OracleError(rc)
     return out.reshape(B, hq, d) if decode else out
+
+
+def attend_prefix(q, k, v, seqlens=None, qlens=None, segs=None, window=None, scale=None,
+                  want_probs=False, want_records=False):
+    """Queries against a cached prefix: q [B,Hq,Tq,d], k/v [B,Hkv,C,d] ->
+    out [B,Tq,Hq,d].  seqlens: cells s_b in the cache (new ones included);
+    qlens: new query rows t_b; segs [B,Tq]: each query row's segment start.
+    Query row i sits at position s_b - t_b + i."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, hq, tq, d = q.shape
+    _, hkv, C, _ = k.shape
+    w = -1 if window is None else int(window)
+    sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((B, tq, hq, d), np.float64)
+    probs = np.zeros((B, hq, tq, C), np.float64) if want_probs else None
+    rec = np.zeros((B, tq, hq, 5), np.int32) if want_records else None
+    sl, ql = _seq(seqlens), _seq(qlens)
+    sg = None if segs is None else np.ascontiguousarray(np.asarray(segs, dtype=np.int32))
+    if sg is not None and sg.shape != (B, tq):
+        raise ValueError("segs must be [B, Tq]")
+    rc = lib().oracle_attend_prefix(_dp(q), _dp(k), _dp(v), _dp(out),
+                                    _dp(probs) if probs is not None else None, _ip(rec),
+                                    _ip(sl), _ip(ql), _ip(sg), B, tq, C, hq, hkv, d, w, sc)
+    if rc:
+        raise OracleError(rc)
+    return out, probs, rec
+
+
+def decode_cache(q, k, v, knew=None, vnew=None, seqlens=None, window=None, scale=None,
+                 ring=False, want_records=False):
+    """Decode that first commits a candidate (knew/vnew [B,Hkv,d]) at cell
+    n_b - 1 and/or addresses a rolling cache (cell j in slot j mod C).
+    Returns (out [B,Hq,d], updated k, updated v, records or None); the
+    inputs are not modified."""
+    q = _f64(q)
+    k, v = _f64(k).copy(), _f64(v).copy()
+    B, hq, d = q.shape
+    _, hkv, C, _ = k.shape
+    if (knew is None) != (vnew is None):
+        raise ValueError("knew and vnew go together")
+    kn = None if knew is None else _f64(knew)
+    vn = None if vnew is None else _f64(vnew)
+    w = -1 if window is None else int(window)
+    sc = 1.0 / np.sqrt(d) if scale is None else float(scale)
+    out = np.zeros((B, hq, d), np.float64)
+    rec = np.zeros((B, hq, 5), np.int32) if want_records else None
+    sl = _seq(seqlens)
+    rc = lib().oracle_decode_cache(_dp(q), _dp(k), _dp(v),
+                                   _dp(kn) if kn is not None else None,
+                                   _dp(vn) if vn is not None else None, _dp(out), _ip(rec),
+                                   _ip(sl), B, C, hq, hkv, d, w, sc, int(bool(ring)))
+    if rc:
+        raise OracleError(rc)
+    return out, k, v, rec

@@ -83,3 +83,59 @@ def decode(q, k, v, seqlens=None, window=None, scale=None):
             keys = permitted(n - 1, n, window, C) if n > 0 else []
             out[b][h], _ = attend(q[b][h], k[b][g], v[b][g], keys, sc)
     return out
+
+
+def prefix(q, k, v, seqlens=None, qlens=None, segs=None, window=None, scale=None):
+    """Queries against a cached prefix, by membership tests.
+
+    q nested [B][Hq][Tq][d], k/v [B][Hkv][C][d] -> out [B][Tq][Hq][d].  Query
+    row i of t_b new ones sits at position p = s_b - t_b + i ("How do you
+    implement grouped query attention (GQA)?", section "Worked example": the
+    tril(s - t) mask); key j is permitted when j <= p, j is not before the
+    row's segment start and p - j < w (section "Intersect the window with the
+    context already permitted")."""
+    B, hq, T, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    hkv, C = len(k[0]), len(k[0][0])
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    out = [[[None] * hq for _ in range(T)] for _ in range(B)]
+    for b in range(B):
+        s = C if seqlens is None else seqlens[b]
+        t = T if qlens is None else qlens[b]
+        for h in range(hq):
+            g = group_of(h, hq, hkv)
+            for i in range(T):
+                p = s - t + i
+                seg = 0 if segs is None else segs[b][i]
+                keys = []
+                if i < t:
+                    for j in range(C):
+                        if j > p or j < seg:
+                            continue
+                        if window is not None and p - j >= window:
+                            continue
+                        keys.append(j)
+                out[b][i][h], _ = attend(q[b][h][i], k[b][g], v[b][g], keys, sc)
+    return out
+
+
+def decode_ring(q, k, v, seqlens, window, scale=None):
+    """Decode over a rolling cache: the cell with index j lives in slot j mod C
+    (the rolling buffer of the Mistral 7B paragraph in "Share key/value heads
+    and make context explicit").  The logical cells are looked up one by one
+    from their slots; the permitted ones are those within the window."""
+    B, hq, d = len(q), len(q[0]), len(q[0][0])
+    hkv, C = len(k[0]), len(k[0][0])
+    sc = 1.0 / math.sqrt(d) if scale is None else scale
+    out = [[None] * hq for _ in range(B)]
+    for b in range(B):
+        n = seqlens[b]
+        for h in range(hq):
+            g = group_of(h, hq, hkv)
+            cells_k, cells_v, keys = {}, {}, []
+            for j in range(n):
+                if n - 1 - j < window:
+                    keys.append(j)
+                    cells_k[j] = k[b][g][j % C]
+                    cells_v[j] = v[b][g][j % C]
+            out[b][h], _ = attend(q[b][h], cells_k, cells_v, keys, sc)
+    return out

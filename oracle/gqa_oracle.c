@@ -49,6 +49,21 @@
  *             pairs heads with the wrong KV head.
  *  [BYTES]    "GQA, FlashAttention and the KV cache", section "Computing the
  *             cache requirement": M_KV = 2 L B T Hkv d e bytes.
+ *  [SEGMENT]  "Share key/value heads and make context explicit", section
+ *             "Intersect the window with the context already permitted": the
+ *             query's own segment start s_{b,t} bounds its keys from below
+ *             and is intersected with the window (six packed cells: at cell 4
+ *             the segment starts at 2 and the window at 3; at cell 5 a new
+ *             segment starts, leaving only self).
+ *  [CANDIDATE] "Extend the existing full and cached attention paths": the
+ *             incremental step reads the new (candidate) key and value from
+ *             their own buffers at the new position and commits them to the
+ *             cache as part of the same step.
+ *  [ROLLING]  "Share key/value heads and make context explicit", the
+ *             paragraph on the Mistral 7B report: sliding-window attention
+ *             over a rolling buffer that overwrites the oldest entries; a
+ *             buffer of capacity w holds every key a window of w reaches,
+ *             cell j in slot j mod w.
  *
  * Layouts (d innermost, contiguous):
  *   prefill: q [B,Hq,T,d], k and v [B,Hkv,C,d], out [B,T,Hq,d] (the merged
@@ -404,5 +419,174 @@ int oracle_expanded(const double *q, const double *k, const double *v, double *o
     free(vx);
     free(keep);
     free(sc);
+    return ORACLE_OK;
+}
+
+/*
+ * Queries against a cached prefix [MASKOFF][WINDOW][SEGMENT][SOFTMAX].
+ * q is [B,Hq,Tq,d]; out is [B,Tq,Hq,d].  seqlens (nullable => every s_b = C)
+ * is the number s_b of cells in the cache, the new ones included; qlens
+ * (nullable => every t_b = Tq) is the number t_b <= Tq of new query rows of
+ * batch row b.  Query row i < t_b sits at absolute position p = s_b - t_b + i
+ * (bottom-right alignment) and reads keys lo..p, where lo is
+ * causal_window_start(p, seg, w) with seg = segs[b,i] (nullable => 0), and
+ * lo = seg without a window.  A row is inactive, with zero output and the
+ * {g,-1,-1,0,0} record, when i >= t_b, when p < 0 (a query placed before the
+ * first cell) or when its segment starts after it (seg > p, where the window
+ * rule gives no start).  probs (nullable) is [B,Hq,Tq,C]; rec (nullable) is
+ * [B,Tq,Hq,5].
+ *
+ * With t_b = s_b = n_b and no segments this is oracle_prefill; with Tq = 1
+ * and t_b = 1 it is oracle_decode.
+ */
+int oracle_attend_prefix(const double *q, const double *k, const double *v, double *out,
+                         double *probs, int32_t *rec, const int32_t *seqlens,
+                         const int32_t *qlens, const int32_t *segs, int B, int Tq, int C,
+                         int hq, int hkv, int d, int window, double scale)
+{
+    int rc = check_heads(hq, hkv);
+    if (rc)
+        return rc;
+    if (window == 0)
+        return ORACLE_ERR_ZERO_WINDOW;
+    if (B < 0 || Tq < 0 || C < 0 || d <= 0 || Tq > C)
+        return ORACLE_ERR_SHAPE;
+    for (int b = 0; b < B; ++b) {
+        int sb = seqlens ? seqlens[b] : C;
+        int tb = qlens ? qlens[b] : Tq;
+        if (sb < 0 || sb > C || tb < 0 || tb > Tq)
+            return ORACLE_ERR_SHAPE;
+    }
+    if (probs)
+        memset(probs, 0, sizeof(double) * (size_t)B * hq * Tq * C);
+    const int64_t rows = (int64_t)B * hq;
+#pragma omp parallel
+    {
+        double *scratch = (double *)malloc(sizeof(double) * (size_t)(C > 0 ? C : 1));
+#pragma omp for schedule(dynamic)
+        for (int64_t bh = 0; bh < rows; ++bh) {
+            int b = (int)(bh / hq), h = (int)(bh % hq);
+            int sb = seqlens ? seqlens[b] : C;
+            int tb = qlens ? qlens[b] : Tq;
+            int64_t g = oracle_kv_head_for_query(h, hq, hkv);
+            const double *krow = k + ((int64_t)b * hkv + g) * C * d;
+            const double *vrow = v + ((int64_t)b * hkv + g) * C * d;
+            for (int i = 0; i < Tq; ++i) {
+                double *z = out + (((int64_t)b * Tq + i) * hq + h) * d;
+                int32_t *r = rec ? rec + (((int64_t)b * Tq + i) * hq + h) * 5 : NULL;
+                int64_t p = (int64_t)sb - tb + i;
+                int64_t seg = segs ? segs[(int64_t)b * Tq + i] : 0;
+                int64_t lo = -1;
+                if (i < tb && p >= 0)
+                    lo = window < 0 ? (seg <= p ? seg : -1) : oracle_window_start(p, seg, window);
+                if (lo < 0) {
+                    for (int c = 0; c < d; ++c)
+                        z[c] = 0.0;
+                    write_record(r, g, 0, 0, 0);
+                    continue;
+                }
+                double *prow = probs ? probs + (((int64_t)b * hq + h) * Tq + i) * C : NULL;
+                attend_row(q + (((int64_t)b * hq + h) * Tq + i) * d, krow, vrow, lo, p, d,
+                           scale, z, prow, scratch);
+                write_record(r, g, lo, p, 1);
+            }
+        }
+        free(scratch);
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * Decode with a candidate and/or a rolling cache [DECODE][CANDIDATE][ROLLING].
+ * q is [B,Hq,d]; k and v are the caches [B,Hkv,C,d]; out is [B,Hq,d].
+ * seqlens (nullable => every n_b = C) counts the cells of the sequence, the
+ * new one included, so the query sits at n_b - 1.
+ *
+ * ring == 0: cell j is stored in slot j, and n_b <= C.
+ * ring != 0: cell j is stored in slot j mod C; the window must satisfy
+ *   1 <= w <= C so that every key the query may read is still held; n_b may
+ *   exceed C.
+ * knew/vnew (both or neither) are the candidate's key and value [B,Hkv,d]:
+ * cell n_b - 1 is first committed to its slot (k and v are updated in
+ * place), then the row attends over the committed cache.  Without a
+ * candidate the cache already holds cell n_b - 1.
+ *
+ * The row reads keys max(0, n_b - w)..n_b - 1 (all of 0..n_b - 1 without a
+ * window), gathered from their slots into a linear copy in ascending cell
+ * order.  n_b = 0 gives a zero row and commits nothing.  rec (nullable) is
+ * [B,Hq,5], in key cells (not slots).
+ */
+int oracle_decode_cache(const double *q, double *k, double *v, const double *knew,
+                        const double *vnew, double *out, int32_t *rec,
+                        const int32_t *seqlens, int B, int C, int hq, int hkv, int d,
+                        int window, double scale, int ring)
+{
+    int rc = check_heads(hq, hkv);
+    if (rc)
+        return rc;
+    if (window == 0)
+        return ORACLE_ERR_ZERO_WINDOW;
+    if (B < 0 || C < 0 || d <= 0 || ((knew == NULL) != (vnew == NULL)))
+        return ORACLE_ERR_SHAPE;
+    if (ring && (window < 1 || window > C))
+        return ORACLE_ERR_SHAPE;
+    int64_t span = 1;
+    for (int b = 0; b < B; ++b) {
+        int nb = seqlens ? seqlens[b] : C;
+        if (nb < 0 || (!ring && nb > C))
+            return ORACLE_ERR_SHAPE;
+        if (nb > span)
+            span = nb;
+    }
+    /* Commit each candidate (one per KV head of a batch row) to its slot. */
+    if (knew)
+        for (int b = 0; b < B; ++b) {
+            int nb = seqlens ? seqlens[b] : C;
+            if (nb == 0)
+                continue;
+            int64_t slot = ring ? (int64_t)(nb - 1) % C : nb - 1;
+            for (int g = 0; g < hkv; ++g) {
+                size_t dst = (((size_t)b * hkv + g) * C + slot) * d;
+                size_t src = ((size_t)b * hkv + g) * d;
+                memcpy(k + dst, knew + src, sizeof(double) * d);
+                memcpy(v + dst, vnew + src, sizeof(double) * d);
+            }
+        }
+    const int64_t rows = (int64_t)B * hq;
+#pragma omp parallel
+    {
+        double *kl = (double *)malloc(sizeof(double) * (size_t)span * d);
+        double *vl = (double *)malloc(sizeof(double) * (size_t)span * d);
+        double *scratch = (double *)malloc(sizeof(double) * (size_t)span);
+#pragma omp for schedule(dynamic)
+        for (int64_t bh = 0; bh < rows; ++bh) {
+            int b = (int)(bh / hq), h = (int)(bh % hq);
+            int nb = seqlens ? seqlens[b] : C;
+            int64_t g = oracle_kv_head_for_query(h, hq, hkv);
+            double *z = out + bh * d;
+            int32_t *r = rec ? rec + bh * 5 : NULL;
+            if (nb == 0) {
+                for (int c = 0; c < d; ++c)
+                    z[c] = 0.0;
+                write_record(r, g, 0, 0, 0);
+                continue;
+            }
+            int64_t t = nb - 1;
+            int64_t lo = window < 0 ? 0 : oracle_window_start(t, 0, window);
+            const double *kc = k + ((int64_t)b * hkv + g) * C * d;
+            const double *vc = v + ((int64_t)b * hkv + g) * C * d;
+            /* Gather cells lo..t from their slots into a linear copy. */
+            for (int64_t j = lo; j <= t; ++j) {
+                int64_t slot = ring ? j % C : j;
+                memcpy(kl + (j - lo) * d, kc + slot * d, sizeof(double) * d);
+                memcpy(vl + (j - lo) * d, vc + slot * d, sizeof(double) * d);
+            }
+            attend_row(q + bh * d, kl, vl, 0, t - lo, d, scale, z, NULL, scratch);
+            write_record(r, g, lo, t, 1);
+        }
+        free(kl);
+        free(vl);
+        free(scratch);
+    }
     return ORACLE_OK;
 }

@@ -13,6 +13,7 @@ import subprocess
 import pytest
 
 import oracle
+from tests import test_oracle_next as next_pins
 from tests import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gqa_oracle.c")
@@ -71,22 +72,67 @@ def _build_mutant(tmp_path, name, old, new):
     return str(lib)
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_mutant(name, tmp_path, golden_dir, monkeypatch):
-    old, new = MUTANTS[name]
+# Mistakes in the functions for queries against a cached prefix, packed
+# segments, the candidate commit and the rolling cache.  (Only mutants that
+# keep every access in bounds: a mutant runs inside the test process.)
+MUTANTS_NEXT = {
+    # the pages' own cache mask bug: queries aligned to the top left
+    "prefix_top_left_alignment": ("int64_t p = (int64_t)sb - tb + i;", "int64_t p = i;"),
+    "prefix_segment_ignored": ("int64_t seg = segs ? segs[(int64_t)b * Tq + i] : 0;",
+                               "int64_t seg = 0;"),
+    "prefix_window_drops_segment": ("oracle_window_start(p, seg, window)",
+                                    "oracle_window_start(p, 0, window)"),
+    "ring_slot_shifted": ("int64_t slot = ring ? j % C : j;",
+                          "int64_t slot = ring ? (j + 1) % C : j;"),
+    "candidate_one_cell_late": ("int64_t slot = ring ? (int64_t)(nb - 1) % C : nb - 1;",
+                                "int64_t slot = ring ? (int64_t)nb % C : (nb < C ? nb : nb - 1);"),
+    "candidate_value_not_committed": ("memcpy(v + dst, vnew + src, sizeof(double) * d);", ""),
+}
+
+PINS_NEXT = [
+    ("test_prefix_full_prompt_equals_prefill", False),
+    ("test_prefix_one_token_equals_decode", False),
+    ("test_prefix_printed_last_row", True),
+    ("test_prefix_matches_dense_tril_mask", False),
+    ("test_prefix_matches_brute_force", False),
+    ("test_packed_segments_stated_cells", True),
+    ("test_packing_equals_separate_sequences", False),
+    ("test_candidate_commit_is_exact_and_local", False),
+    ("test_candidate_is_seen_by_its_own_query", False),
+    ("test_ring_equals_linear_window", False),
+    ("test_ring_streaming_appends", False),
+]
+
+ORACLE_FUNCTIONS = ("oracle_kv_head_for_query", "oracle_window_start", "oracle_kv_cache_bytes",
+                    "oracle_prefill", "oracle_decode", "oracle_expanded",
+                    "oracle_attend_prefix", "oracle_decode_cache")
+
+
+def _run_pins(name, old, new, module, pin_list, tmp_path, golden_dir, monkeypatch):
     path = _build_mutant(tmp_path, name, old, new)
     real = oracle.lib()
     mutant = ctypes.CDLL(path)
-    for fn in ("oracle_kv_head_for_query", "oracle_window_start", "oracle_kv_cache_bytes",
-               "oracle_prefill", "oracle_decode", "oracle_expanded"):
+    for fn in ORACLE_FUNCTIONS:
         getattr(mutant, fn).argtypes = getattr(real, fn).argtypes
         getattr(mutant, fn).restype = getattr(real, fn).restype
     monkeypatch.setattr(oracle, "_lib", mutant)
     failed = []
-    for pin, wants_golden in PINS:
-        f = getattr(pins, pin)
+    for pin, wants_golden in pin_list:
+        f = getattr(module, pin)
         try:
             f(golden_dir) if wants_golden else f()
         except (AssertionError, oracle.OracleError):
             failed.append(pin)
     assert failed, f"mutant {name} survived every pin"
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path, golden_dir, monkeypatch):
+    old, new = MUTANTS[name]
+    _run_pins(name, old, new, pins, PINS, tmp_path, golden_dir, monkeypatch)
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS_NEXT))
+def test_next_pins_catch_mutant(name, tmp_path, golden_dir, monkeypatch):
+    old, new = MUTANTS_NEXT[name]
+    _run_pins(name, old, new, next_pins, PINS_NEXT, tmp_path, golden_dir, monkeypatch)
