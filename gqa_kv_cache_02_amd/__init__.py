@@ -6,8 +6,10 @@ step of the computation runs in the library's HIP kernels; there is no CPU or
 PyTorch fallback, and every entry point raises if the library is missing.
 
 Layouts (contiguous, d innermost):
-    prefill: q [B, Hq, T, d], k/v [B, Hkv, C, d] -> out [B, T, Hq, d]
-    decode:  q [B, Hq, d],    k/v [B, Hkv, C, d] -> out [B, Hq, d]
+    prefill:        q [B, Hq, T, d],  k/v [B, Hkv, C, d] -> out [B, T, Hq, d]
+    prefill_prefix: q [B, Hq, Tq, d], k/v [B, Hkv, C, d] -> out [B, Tq, Hq, d]
+    decode:         q [B, Hq, d],     k/v [B, Hkv, C, d] -> out [B, Hq, d]
+    decode_cache:   as decode, plus k_new/v_new [B, Hkv, d] and a rolling cache
 ``seqlens`` is an int32 device tensor of per-sequence lengths n_b (decode:
 cells in use including the newly appended one).  ``window=None`` means no local
 window; ``window >= 1`` counts the current cell and at most window-1 earlier
@@ -64,6 +66,10 @@ def _load():
     L.gqa_decode.restype = ctypes.c_int
     L.gqa_decode_records.argtypes = [vp] * 5 + [i32] * 6 + [f32, i32, vp, sz, vp, vp]
     L.gqa_decode_records.restype = ctypes.c_int
+    L.gqa_prefill_prefix.argtypes = [vp] * 7 + [i32] * 7 + [f32, i32, vp, vp]
+    L.gqa_prefill_prefix.restype = ctypes.c_int
+    L.gqa_decode_cache.argtypes = [vp] * 7 + [i32] * 6 + [f32, i32, i32, vp, sz, vp, vp]
+    L.gqa_decode_cache.restype = ctypes.c_int
     L.gqa_prefill_kernel.argtypes = [i32] * 8
     L.gqa_prefill_kernel.restype = ctypes.c_int
     L.gqa_decode_kernel.argtypes = [i32] * 7
@@ -241,4 +247,98 @@ def decode(q, k, v, *, seqlens=None, window=None, scale=None, out=None, workspac
         rc = L.gqa_decode(*args, _stream(dev))
     if rc:
         raise GQAError(rc, "gqa_decode")
+    return out
+
+
+def _rowmeta(name, t, shape, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        t = torch.tensor(t, dtype=torch.int32, device=device)
+    _check_tensor(name, t, torch.int32, device)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def prefill_prefix(q, k, v, *, seqlens=None, qlens=None, seg_starts=None, window=None,
+                   scale=None, out=None, records=None):
+    """Queries against a cached prefix (chunked prefill / several new tokens),
+    optionally with packed segments.  q [B,Hq,Tq,d], k/v [B,Hkv,C,d] ->
+    out [B,Tq,Hq,d].  Query row i of the t_b = qlens[b] new ones sits at cell
+    seqlens[b] - t_b + i; seg_starts [B,Tq] gives each row's segment start."""
+    L = _load()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D")
+    B, hq, Tq, d = q.shape
+    hkv, C = k.shape[1], k.shape[2]
+    if k.shape != (B, hkv, C, d) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, Tq, hq, d), dtype=q.dtype, device=dev)
+    _check_tensor("out", out, q.dtype, dev)
+    if out.shape != (B, Tq, hq, d):
+        raise ValueError("out must be [B,Tq,Hq,d]")
+    sl = _rowmeta("seqlens", seqlens, (B,), dev)
+    ql = _rowmeta("qlens", qlens, (B,), dev)
+    sg = _rowmeta("seg_starts", seg_starts, (B, Tq), dev)
+    if records is not None:
+        _check_tensor("records", records, torch.int32, dev)
+        if records.shape != (B, Tq, hq, 5):
+            raise ValueError("records must be int32 [B,Tq,Hq,5]")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = L.gqa_prefill_prefix(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sl), _ptr(ql),
+                              _ptr(sg), B, Tq, C, hq, hkv, d, _win(window), sc, _dt(q.dtype),
+                              _ptr(records), _stream(dev))
+    if rc:
+        raise GQAError(rc, "gqa_prefill_prefix")
+    return out
+
+
+def decode_cache(q, k, v, *, k_new=None, v_new=None, seqlens=None, window=None, ring=False,
+                 scale=None, out=None, workspace=None, records=None):
+    """Decode that reads the new cell from k_new/v_new [B,Hkv,d] and commits
+    them to the cache (k and v are updated in place), and/or addresses a
+    rolling cache (ring=True: cell j in slot j mod C, 1 <= window <= C)."""
+    L = _load()
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be 3-D and k, v 4-D")
+    B, hq, d = q.shape
+    hkv, C = k.shape[1], k.shape[2]
+    if k.shape != (B, hkv, C, d) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.dtype, dev)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t is not None:
+            _check_tensor(name, t, q.dtype, dev)
+            if t.shape != (B, hkv, d):
+                raise ValueError(f"{name} must be [B,Hkv,d]")
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=q.dtype, device=dev)
+    _check_tensor("out", out, q.dtype, dev)
+    if out.shape != (B, hq, d):
+        raise ValueError("out must be [B,Hq,d]")
+    sl = _rowmeta("seqlens", seqlens, (B,), dev)
+    if records is not None:
+        _check_tensor("records", records, torch.int32, dev)
+        if records.shape != (B, hq, 5):
+            raise ValueError("records must be int32 [B,Hq,5]")
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    w = _win(window)
+    need = int(L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, _dt(q.dtype)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, torch.uint8, dev)
+    rc = L.gqa_decode_cache(_ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(out),
+                            _ptr(sl), B, C, hq, hkv, d, w, sc, _dt(q.dtype), int(bool(ring)),
+                            _ptr(workspace), workspace.numel(), _ptr(records), _stream(dev))
+    if rc:
+        raise GQAError(rc, "gqa_decode_cache")
     return out

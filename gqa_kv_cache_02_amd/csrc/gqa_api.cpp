@@ -90,10 +90,24 @@ int decode_kernel_for(int32_t d, int32_t dtype) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? GQA_OK : GQA_ERR_HIP; }
 
+// Extra inputs of the prefix-query and cache-update forms.
+struct PrefixExtra {
+    bool prefix = false;
+    const int32_t *qlens = nullptr;
+    const int32_t *segs = nullptr;
+};
+struct CacheExtra {
+    const void *knew = nullptr;
+    const void *vnew = nullptr;
+    void *kw = nullptr;
+    void *vw = nullptr;
+    bool ring = false;
+};
+
 int prefill_impl(const void *q, const void *k, const void *v, void *out, const int32_t *seqlens,
                  int32_t B, int32_t T, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
                  int32_t window, float scale, int32_t dtype, int32_t *records, bool want_records,
-                 void *stream) {
+                 void *stream, const PrefixExtra &x = PrefixExtra()) {
     int rc = check_scalars(Hq, Hkv, d, window, scale, dtype);
     if (rc)
         return rc;
@@ -105,6 +119,8 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
         return GQA_OK;
     if ((rc = check_pointers(q, k, v, out, seqlens, dtype, true)))
         return rc;
+    if ((x.qlens && !aligned(x.qlens, 4)) || (x.segs && !aligned(x.segs, 4)))
+        return GQA_ERR_ALIGN;
     if (want_records) {
         if (!records)
             return GQA_ERR_NULL;
@@ -114,6 +130,9 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
     const int r = Hq / Hkv;
     Problem p{q, k, v, out, seqlens, want_records ? records : nullptr,
               B, T, C, Hq, Hkv, d, window, scale, dtype, false};
+    p.prefix = x.prefix;
+    p.qlens = x.qlens;
+    p.segs = x.segs;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (prefill_kernel_for(d, dtype) == GQA_KERNEL_PREFILL_MFMA && fast_aligned(q, k, v, out)) {
         if (!gqa::prefill_grid_ok(B, T, Hq, Hkv))
@@ -128,11 +147,15 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
 int decode_impl(const void *q, const void *k, const void *v, void *out, const int32_t *seqlens,
                 int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t d, int32_t window,
                 float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
-                int32_t *records, bool want_records, void *stream) {
+                int32_t *records, bool want_records, void *stream,
+                const CacheExtra &x = CacheExtra()) {
     int rc = check_scalars(Hq, Hkv, d, window, scale, dtype);
     if (rc)
         return rc;
     if (B < 0 || C < 0)
+        return GQA_ERR_SHAPE;
+    // a rolling cache must hold every cell the window reaches
+    if (x.ring && (window < 1 || window > C))
         return GQA_ERR_SHAPE;
     if ((rc = check_sizes(B, Hq, Hkv, 1, C, d, dtype)))
         return rc;
@@ -140,6 +163,11 @@ int decode_impl(const void *q, const void *k, const void *v, void *out, const in
         return GQA_OK;
     if ((rc = check_pointers(q, k, v, out, seqlens, dtype, C > 0)))
         return rc;
+    if ((x.knew == nullptr) != (x.vnew == nullptr))
+        return GQA_ERR_NULL;
+    const uintptr_t es = static_cast<uintptr_t>(elem_size(dtype));
+    if (x.knew && (!aligned(x.knew, es) || !aligned(x.vnew, es)))
+        return GQA_ERR_ALIGN;
     if (want_records) {
         if (!records)
             return GQA_ERR_NULL;
@@ -148,9 +176,16 @@ int decode_impl(const void *q, const void *k, const void *v, void *out, const in
     }
     Problem p{q, k, v, out, seqlens, want_records ? records : nullptr,
               B, 1, C, Hq, Hkv, d, window, scale, dtype, true};
+    p.knew = x.knew;
+    p.vnew = x.vnew;
+    p.kw = x.kw;
+    p.vw = x.vw;
+    p.ring = x.ring;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int r = Hq / Hkv;
-    if (decode_kernel_for(d, dtype) == GQA_KERNEL_DECODE_SPLIT && fast_aligned(q, k, v, out)) {
+    const bool cand_aligned = !x.knew || (aligned(x.knew, 16) && aligned(x.vnew, 16));
+    if (decode_kernel_for(d, dtype) == GQA_KERNEL_DECODE_SPLIT && fast_aligned(q, k, v, out) &&
+        cand_aligned) {
         const gqa::DecodePlan plan = gqa::plan_decode(B, C, Hq, Hkv, d, window);
         if (B > kMaxGridYZ || (int64_t)Hkv * plan.nhc > kMaxGridYZ)
             return GQA_ERR_SHAPE;
@@ -211,6 +246,36 @@ int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, 
                        size_t workspace_bytes, int32_t *records, void *stream) {
     return decode_impl(q, k_cache, v_cache, out, seqlens, B, C, Hq, Hkv, d, window, scale, dtype,
                        workspace, workspace_bytes, records, true, stream);
+}
+
+int gqa_prefill_prefix(const void *q, const void *k_cache, const void *v_cache, void *out,
+                       const int32_t *seqlens, const int32_t *qlens, const int32_t *seg_starts,
+                       int32_t B, int32_t Tq, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
+                       int32_t window, float scale, int32_t dtype, int32_t *records,
+                       void *stream) {
+    PrefixExtra x;
+    x.prefix = true;
+    x.qlens = qlens;
+    x.segs = seg_starts;
+    return prefill_impl(q, k_cache, v_cache, out, seqlens, B, Tq, C, Hq, Hkv, d, window, scale,
+                        dtype, records, records != nullptr, stream, x);
+}
+
+int gqa_decode_cache(const void *q, void *k_cache, void *v_cache, const void *k_new,
+                     const void *v_new, void *out, const int32_t *seqlens, int32_t B, int32_t C,
+                     int32_t Hq, int32_t Hkv, int32_t d, int32_t window, float scale,
+                     int32_t dtype, int32_t ring, void *workspace, size_t workspace_bytes,
+                     int32_t *records, void *stream) {
+    if (ring != 0 && ring != 1)
+        return GQA_ERR_SHAPE;
+    CacheExtra x;
+    x.knew = k_new;
+    x.vnew = v_new;
+    x.kw = k_cache;
+    x.vw = v_cache;
+    x.ring = ring != 0;
+    return decode_impl(q, k_cache, v_cache, out, seqlens, B, C, Hq, Hkv, d, window, scale, dtype,
+                       workspace, workspace_bytes, records, records != nullptr, stream, x);
 }
 
 int gqa_prefill_kernel(int32_t B, int32_t T, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,

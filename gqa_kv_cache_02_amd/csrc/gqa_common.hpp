@@ -59,6 +59,19 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+__device__ __forceinline__ int wave_min_i(int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        x = min(x, __shfl_xor(x, m, 64));
+    return x;
+}
+__device__ __forceinline__ int wave_max_i(int x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1)
+        x = max(x, __shfl_xor(x, m, 64));
+    return x;
+}
+
 // Window lower bound for a query at cell t (segment start 0): the current
 // cell plus at most window-1 earlier cells; window < 0 means none.
 __device__ __forceinline__ int window_lo(int t, int window) {
@@ -66,6 +79,18 @@ __device__ __forceinline__ int window_lo(int t, int window) {
         return 0;
     int lo = t - (window - 1);
     return lo > 0 ? lo : 0;
+}
+
+// Lower bound of the permitted keys of a query at cell p whose segment
+// starts at cell seg: the later of the segment start and the window start
+// ("Share key/value heads and make context explicit", section "Intersect the
+// window with the context already permitted").  -1 when the segment starts
+// after the query (no permitted key).
+__device__ __forceinline__ int segment_lo(int p, int seg, int window) {
+    if (seg > p)
+        return -1;
+    const int w = window_lo(p, window);
+    return seg > w ? seg : w;
 }
 
 } // namespace gqa

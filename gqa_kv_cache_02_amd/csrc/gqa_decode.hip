@@ -33,6 +33,14 @@
 // softmax with a numerically stable running normalisation gives the dense
 // result).  The kernel boundary orders the two steps; no workgroup waits on
 // another.
+//
+// The extended instantiation (kExt) adds two cache forms.  A candidate: the
+// new cell n_b - 1 is read from its own key/value buffers and committed to
+// its cache slot in the same launch, as the incremental step of "Extend the
+// existing full and cached attention paths" includes the candidate key before
+// the cache commits.  A rolling cache: cell j lives in slot j mod C (the
+// rolling buffer of the Mistral 7B paragraph in "Share key/value heads and
+// make context explicit"), with a window of at most C cells.
 #include <limits.h>
 
 #include "gqa_common.hpp"
@@ -55,6 +63,12 @@ struct DecodeArgs {
     int32_t *rec_part;  // [B, Hq, nsplit, 4] (record instantiation only)
     int C, Hq, Hkv, window, r, nhc, nsplit, chunk;
     float scale_log2;
+    // kExt only
+    const uint16_t *knew; // [B, Hkv, D] candidate key (nullable)
+    const uint16_t *vnew; // [B, Hkv, D] candidate value
+    uint16_t *kw;         // the K/V caches again, writable, for the commit
+    uint16_t *vw;
+    int ring;             // cell j in slot j mod C
 };
 
 template <int D> struct DecodeSmem {
@@ -71,7 +85,7 @@ __device__ __forceinline__ s16x4 ds_read_tr_d(const uint16_t *p) {
         (__attribute__((address_space(3))) s16x4 *)(p));
 }
 
-template <int D, bool kRecord>
+template <int D, bool kRecord, bool kExt>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;               // 32-feature k-steps of Q.K
     constexpr int DB = D / 16;               // 16-column blocks of P.V
@@ -137,6 +151,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int64_t lane_off = ((int64_t)b * a.Hkv + g) * (int64_t)a.C * D;
     const uint16_t *kbase = a.k + lane_off;
     const uint16_t *vbase = a.v + lane_off;
+
+    // Cache row of key cell `key` (relative to kbase/vbase), and where the
+    // candidate cell reads from.  In a rolling cache the permitted cells
+    // lo..hi (fewer than C of them) map to slots key - base or key - base - C
+    // with base = C * floor(lo / C).
+    const uint16_t *kcand = nullptr, *vcand = nullptr;
+    int ring_base = 0;
+    if constexpr (kExt) {
+        if (a.ring)
+            ring_base = (lo / a.C) * a.C;
+        if (a.knew) {
+            kcand = a.knew + ((int64_t)b * a.Hkv + g) * D;
+            vcand = a.vnew + ((int64_t)b * a.Hkv + g) * D;
+            // Commit by the workgroup whose chunk holds the new cell (first
+            // head chunk only).  No workgroup of this launch reads that slot:
+            // the new cell is read from the candidate buffers, and the cell
+            // the slot held before (hi - C, rolling cache) is outside the
+            // window.
+            if (hc == 0 && c_hi == hi && tid < D / 8) {
+                int64_t slot = hi;
+                if (a.ring)
+                    slot = hi - ring_base >= a.C ? hi - ring_base - a.C : hi - ring_base;
+                *reinterpret_cast<uint4 *>(a.kw + lane_off + slot * D + tid * 8) =
+                    *reinterpret_cast<const uint4 *>(kcand + tid * 8);
+                *reinterpret_cast<uint4 *>(a.vw + lane_off + slot * D + tid * 8) =
+                    *reinterpret_cast<const uint4 *>(vcand + tid * 8);
+            }
+        }
+    }
+    auto cell = [&](int key) -> int64_t {
+        if constexpr (kExt) {
+            if (a.ring) {
+                const int sl = key - ring_base;
+                return sl >= a.C ? sl - a.C : sl;
+            }
+        }
+        return key;
+    };
     uint16_t *vs = reinterpret_cast<uint16_t *>(smem) + wave * kDecodeTile * LDV;
 
     // One tile's loads: K in the MFMA operand layout (lane (hl, qg) of key
@@ -147,7 +199,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const int key = j0 + kb * 16 + hl;
-            const uint16_t *krow = kbase + (int64_t)key * D + qg * 8;
+            const uint16_t *krow = kbase + cell(key) * D + qg * 8;
+            if constexpr (kExt)
+                if (kcand && key == hi)
+                    krow = kcand + qg * 8;
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 if (key <= c_hi)
@@ -161,9 +216,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         for (int it = 0; it < VIT; ++it) {
             const int key = j0 + it * VPI + lane / LPK;
             const int col = (lane % LPK) * 8;
+            const uint16_t *vrow = vbase + cell(key) * D;
+            if constexpr (kExt)
+                if (vcand && key == hi)
+                    vrow = vcand;
             if (key <= c_hi)
-                vr[it] = __builtin_nontemporal_load(
-                    reinterpret_cast<const u32x4 *>(vbase + (int64_t)key * D + col));
+                vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow + col));
             else
                 vr[it] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -467,7 +525,7 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window) {
     return p;
 }
 
-template <int D, bool kRecord>
+template <int D, bool kRecord, bool kExt>
 static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, hipStream_t s) {
     unsigned char *w = static_cast<unsigned char *>(ws);
     DecodeArgs a;
@@ -483,9 +541,14 @@ static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, h
     a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
     a.r = p.Hq / p.Hkv; a.nhc = plan.nhc; a.nsplit = plan.nsplit; a.chunk = plan.chunk;
     a.scale_log2 = p.scale * kLog2e;
+    a.knew = static_cast<const uint16_t *>(p.knew);
+    a.vnew = static_cast<const uint16_t *>(p.vnew);
+    a.kw = static_cast<uint16_t *>(p.kw);
+    a.vw = static_cast<uint16_t *>(p.vw);
+    a.ring = p.ring ? 1 : 0;
     // at least one split so that empty rows still get their zero output
     dim3 grid(plan.nsplit > 0 ? plan.nsplit : 1, p.Hkv * plan.nhc, p.B);
-    decode_kernel<D, kRecord><<<grid, 256, 0, s>>>(a);
+    decode_kernel<D, kRecord, kExt><<<grid, 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.nsplit <= 1)
         return e; // every row finished inside the split kernel
@@ -502,11 +565,19 @@ static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, h
 hipError_t launch_decode_split(const Problem &p, const DecodePlan &plan, void *workspace,
                                hipStream_t stream) {
     const bool rec = p.records != nullptr;
-    if (p.d == 128)
-        return rec ? launch_d<128, true>(p, plan, workspace, stream)
-                   : launch_d<128, false>(p, plan, workspace, stream);
-    return rec ? launch_d<64, true>(p, plan, workspace, stream)
-               : launch_d<64, false>(p, plan, workspace, stream);
+    const bool ext = p.ring || p.knew != nullptr;
+    if (p.d == 128) {
+        if (ext)
+            return rec ? launch_d<128, true, true>(p, plan, workspace, stream)
+                       : launch_d<128, false, true>(p, plan, workspace, stream);
+        return rec ? launch_d<128, true, false>(p, plan, workspace, stream)
+                   : launch_d<128, false, false>(p, plan, workspace, stream);
+    }
+    if (ext)
+        return rec ? launch_d<64, true, true>(p, plan, workspace, stream)
+                   : launch_d<64, false, true>(p, plan, workspace, stream);
+    return rec ? launch_d<64, true, false>(p, plan, workspace, stream)
+               : launch_d<64, false, false>(p, plan, workspace, stream);
 }
 
 } // namespace gqa

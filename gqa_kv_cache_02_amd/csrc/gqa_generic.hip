@@ -1,6 +1,11 @@
 // gqa_generic.hip -- the general kernel: fp32 or bf16 storage, any head width
 // d <= 256, decode or causal prefill, optional window.
 //
+// Prefill rows may be queries against a cached prefix (row i of the t_b new
+// ones at cell s_b - t_b + i) with a per-row segment start; decode may read
+// the new cell from a separate candidate buffer and commit it, and may
+// address a rolling cache (cell j in slot j mod C).
+//
 // One 64-lane wavefront owns one output row t of one batch row b and up to
 // kGroupHeads query heads of one KV group g.  Lane c holds features
 // c, c+64, c+128, c+192.  Each permitted key cell is loaded from HBM once per
@@ -24,10 +29,16 @@ struct GenericArgs {
     const void *v;
     void *out;
     const int32_t *seqlens;
+    const int32_t *qlens;
+    const int32_t *segs;
     int32_t *records;
+    const void *knew;
+    const void *vnew;
+    void *kw;
+    void *vw;
     int T, C, Hq, Hkv, d, window, r, nchunk;
     float scale_log2;
-    int decode;
+    int decode, prefix, ring;
 };
 
 template <typename T, int DPL, bool kRecord>
@@ -40,17 +51,51 @@ __global__ __launch_bounds__(64) void generic_kernel(GenericArgs a) {
     int nh = a.r - chunk * kGroupHeads;
     nh = nh < kGroupHeads ? nh : kGroupHeads;
 
-    const int nb = a.seqlens ? a.seqlens[b] : (a.decode ? a.C : a.T);
-    const int t = a.decode ? nb - 1 : static_cast<int>(blockIdx.x);
-    const bool active = a.decode ? (nb >= 1) : (t < nb);
     const int tq = a.decode ? 1 : a.T;         // query rows per (b, h)
-    const int trow = a.decode ? 0 : t;         // row index within q/out
+    const int trow = a.decode ? 0 : static_cast<int>(blockIdx.x); // row within q/out
     const int d = a.d;
+    // t: the query's cell; lo: its first permitted key
+    int t, lo;
+    bool active;
+    if (a.decode) {
+        const int nb = a.seqlens ? a.seqlens[b] : a.C;
+        t = nb - 1;
+        active = nb >= 1;
+        lo = window_lo(t, a.window);
+    } else {
+        int s_b, t_b;
+        if (a.prefix) {
+            s_b = a.seqlens ? a.seqlens[b] : a.C;
+            t_b = a.qlens ? a.qlens[b] : a.T;
+        } else {
+            s_b = a.seqlens ? a.seqlens[b] : a.T;
+            t_b = s_b;
+        }
+        t = s_b - t_b + trow;
+        const int seg = a.segs ? a.segs[(int64_t)b * a.T + trow] : 0;
+        lo = segment_lo(t, seg, a.window);
+        active = trow < t_b && t >= 0 && lo >= 0;
+    }
 
     const T *q = static_cast<const T *>(a.q);
     const T *kc = static_cast<const T *>(a.k) + ((int64_t)b * a.Hkv + g) * a.C * d;
     const T *vc = static_cast<const T *>(a.v) + ((int64_t)b * a.Hkv + g) * a.C * d;
     T *out = static_cast<T *>(a.out);
+    // The candidate (decode): cell t is read from its own buffer and, by the
+    // first head chunk of the group, committed to its cache slot.  Nothing
+    // else in this launch reads that slot: the cell it held before (t - C in
+    // a rolling cache) is outside the window.
+    const T *kcand = a.knew ? static_cast<const T *>(a.knew) + ((int64_t)b * a.Hkv + g) * d : nullptr;
+    const T *vcand = a.vnew ? static_cast<const T *>(a.vnew) + ((int64_t)b * a.Hkv + g) * d : nullptr;
+    if (kcand && active && chunk == 0) {
+        const int64_t slot = a.ring ? t % a.C : t;
+        T *kd = static_cast<T *>(a.kw) + (((int64_t)b * a.Hkv + g) * a.C + slot) * d;
+        T *vd = static_cast<T *>(a.vw) + (((int64_t)b * a.Hkv + g) * a.C + slot) * d;
+        for (int c = lane; c < d; c += 64) {
+            kd[c] = kcand[c];
+            vd[c] = vcand[c];
+        }
+    }
 
     if (!active) {
         for (int hh = 0; hh < nh; ++hh) {
@@ -64,8 +109,6 @@ __global__ __launch_bounds__(64) void generic_kernel(GenericArgs a) {
         }
         return;
     }
-
-    const int lo = window_lo(t, a.window);
 
     float qf[kGroupHeads][DPL];
     float acc[kGroupHeads][DPL];
@@ -85,12 +128,18 @@ __global__ __launch_bounds__(64) void generic_kernel(GenericArgs a) {
 
     int rcount = 0, rxor = 0;
     for (int j = lo; j <= t; ++j) {
+        const T *kj = kc + (int64_t)(a.ring ? j % a.C : j) * d;
+        const T *vj = vc + (int64_t)(a.ring ? j % a.C : j) * d;
+        if (kcand && j == t) {
+            kj = kcand;
+            vj = vcand;
+        }
         float kk[DPL], vv[DPL];
 #pragma unroll
         for (int i = 0; i < DPL; ++i) {
             const int c = lane + 64 * i;
-            kk[i] = c < d ? Elem<T>::load(kc + (int64_t)j * d + c) : 0.f;
-            vv[i] = c < d ? Elem<T>::load(vc + (int64_t)j * d + c) : 0.f;
+            kk[i] = c < d ? Elem<T>::load(kj + c) : 0.f;
+            vv[i] = c < d ? Elem<T>::load(vj + c) : 0.f;
         }
 #pragma unroll
         for (int hh = 0; hh < kGroupHeads; ++hh) {
@@ -150,6 +199,8 @@ hipError_t launch_generic(const Problem &p, hipStream_t stream) {
     GenericArgs a;
     a.q = p.q; a.k = p.k; a.v = p.v; a.out = p.out;
     a.seqlens = p.seqlens; a.records = p.records;
+    a.qlens = p.qlens; a.segs = p.segs; a.prefix = p.prefix ? 1 : 0;
+    a.knew = p.knew; a.vnew = p.vnew; a.kw = p.kw; a.vw = p.vw; a.ring = p.ring ? 1 : 0;
     a.T = p.T; a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.d = p.d; a.window = p.window;
     a.r = p.Hq / p.Hkv;
     a.nchunk = (a.r + kGroupHeads - 1) / kGroupHeads;

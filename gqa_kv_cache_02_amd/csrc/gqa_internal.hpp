@@ -15,12 +15,27 @@ struct Problem {
     const void *k;
     const void *v;
     void *out;
-    const int32_t *seqlens; // nullable: n_b = T (prefill) or C (decode)
+    const int32_t *seqlens; // nullable: n_b = T (prefill), C (decode, prefix queries)
     int32_t *records;       // nullable: index-set records
     int B, T, C, Hq, Hkv, d, window;
     float scale;
     int dtype; // 0 fp32, 1 bf16
     bool decode;
+    // Prefill against a cached prefix: query row i of the t_b new ones sits
+    // at cell s_b - t_b + i (s_b = seqlens, default C; t_b = qlens, default
+    // T) and its keys start no earlier than segs[b][i] (default 0).  When
+    // prefix is false, t_b = s_b = n_b and every row i sits at cell i.
+    bool prefix = false;
+    const int32_t *qlens = nullptr;
+    const int32_t *segs = nullptr;
+    // Decode: the candidate's key/value [B,Hkv,d] (both or neither) are read
+    // for cell n_b - 1 and committed to its slot of kw/vw (the same caches
+    // as k/v); ring stores cell j in slot j mod C.
+    const void *knew = nullptr;
+    const void *vnew = nullptr;
+    void *kw = nullptr;
+    void *vw = nullptr;
+    bool ring = false;
 };
 
 // Split-K decode plan: the eligible key range of a row is cut into chunks of

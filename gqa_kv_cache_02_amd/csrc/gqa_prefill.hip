@@ -43,16 +43,15 @@ struct PrefillArgs {
     const uint16_t *v;
     uint16_t *out;
     const int32_t *seqlens;
+    const int32_t *qlens;   // prefix queries only (nullable)
+    const int32_t *segs;    // nullable: segment start of each query row [B,T]
     int32_t *records;
     int B, T, C, Hq, Hkv, window, r, hpw, rb, nhc, nqb;
+    int prefix;             // query rows sit at s_b - t_b + i (else at i, t_b = s_b = n_b)
     float scale_log2; // |scale| * log2(e)
     uint32_t qneg;    // 0x80008000 when scale < 0: Q's sign bits are flipped on load
 };
 
-// LDS row pitches (u16).  K rows are read 16 B per lane, 32 rows at a time:
-// a pitch of 68 dwords spreads 16 consecutive rows over all 64 banks.  V rows
-// are read with ds_read_b64_tr_b16, 4 consecutive rows per 16-lane group: a
-// pitch of 80 dwords puts those rows 16 banks apart.
 // Direct global-to-LDS 16-byte load (lane i lands at lds_addr + 16*i).  It is
 // issued from inline assembly so that the compiler, which cannot tell which
 // LDS bytes the transfer writes, does not put a wait for it in front of every
@@ -133,20 +132,54 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int rows_wg = kPRows * a.rb;
     const int q0 = qblk * rows_wg;
 
-    const int nb = a.seqlens ? a.seqlens[b] : a.T;
     const bool wave_on = wave < nwaves;
     const int hh = wave % a.hpw;            // head within the workgroup
     const int rsub = wave / a.hpw;          // 32-row block within the workgroup
     const int h = g * a.r + hc * a.hpw + hh;
     const int r0 = q0 + rsub * kPRows;
-    const int my_row = r0 + (lane & 31);
+    const int my_row = r0 + (lane & 31);    // query row index (output row)
 
-    // Key range the workgroup needs: from the earliest row's window start to
-    // its last active row.
-    const int wg_last = min(q0 + rows_wg, min(nb, a.T)) - 1;
+    // The row's cell: query row i of the t_b new ones sits at cell
+    // s_b - t_b + i, the offset rule of "How do you implement grouped query
+    // attention (GQA)?", section "Worked example" (a plain prefill has
+    // t_b = s_b = n_b, so row i is cell i).  It reads keys lo..p with lo the
+    // later of its segment start and its window start.
+    int s_b, t_b;
+    if (a.prefix) {
+        s_b = a.seqlens ? a.seqlens[b] : a.C;
+        t_b = a.qlens ? a.qlens[b] : a.T;
+    } else {
+        s_b = a.seqlens ? a.seqlens[b] : a.T;
+        t_b = s_b;
+    }
+    const int my_pos = s_b - t_b + my_row;
+    const int my_seg = (a.segs && my_row < a.T) ? a.segs[(int64_t)b * a.T + my_row] : 0;
+    const int lo_cand = segment_lo(my_pos, my_seg, a.window);
+    const bool row_on = wave_on && my_row < t_b && my_pos >= 0 && lo_cand >= 0;
+    const int lo_row = row_on ? lo_cand : INT_MAX;
+
+    // The wavefront's key range (lanes l and l ^ 32 share a row) and whether
+    // all its rows are active; then the workgroup's, through LDS.
+    const bool w_all = __builtin_amdgcn_ballot_w64(row_on) == ~0ull;
+    const int w_lo = wave_min_i(lo_row);                        // INT_MAX: no active row
+    const int w_lo_last = wave_max_i(row_on ? lo_row : -1);
+    const int w_last = wave_max_i(row_on ? my_pos : -1);        // -1: no active row
+    const int w_first = wave_min_i(row_on ? my_pos : INT_MAX);
+    __shared__ int sm_range[4][2];
+    if (lane == 0) {
+        sm_range[wave][0] = w_lo;
+        sm_range[wave][1] = w_last;
+    }
+    __syncthreads();
+    int wg_lo = INT_MAX, wg_last = -1;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        wg_lo = min(wg_lo, sm_range[w][0]);
+        wg_last = max(wg_last, sm_range[w][1]);
+    }
     const int64_t out_stride = (int64_t)a.Hq * D; // between cells in [B,T,Hq,D]
 
-    if (wg_last < q0) {
+    if (wg_last < 0) {
         // no active row: the whole block is padding, write zeros
         if (wave_on) {
             for (int i = lane; i < kPRows * (D / 4); i += 64) {
@@ -164,14 +197,8 @@ void prefill_mfma_kernel(PrefillArgs a) {
         }
         return;
     }
-    const int wg_lo = window_lo(q0, a.window);
     const int tile_lo = wg_lo / kPBN;
     const int tile_hi = wg_last / kPBN;
-
-    // The wavefront's own key range.
-    const int w_last = min(r0 + kPRows, min(nb, a.T)) - 1; // < r0 when all rows padded
-    const int w_lo = window_lo(r0, a.window);
-    const int w_lo_last = window_lo(r0 + kPRows - 1, a.window);
 
     // Q^T operand, kept for the whole loop: lane l holds row r0 + (l & 31),
     // features s*16 + 8*(l >> 5) .. +8 (sign bits flipped for a negative scale).
@@ -265,7 +292,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
         const unsigned char *kst = src;
         const unsigned char *vst = src + L::kTileBytes;
         const int j0 = tile * kPBN;
-        const bool work = wave_on && w_last >= r0 && j0 <= w_last && j0 + kPBN - 1 >= w_lo;
+        const bool work = w_last >= 0 && j0 <= w_last && j0 + kPBN - 1 >= w_lo;
         // Interior tiles (every key permitted for every row of the wavefront)
         // and edge tiles (diagonal, window edge, padded rows) are separate
         // instantiations so that interior tiles carry no masking code.
@@ -278,16 +305,28 @@ void prefill_mfma_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int e = 0; e < 16; ++e)
                     sacc[kb][e] = 0.f;
+            auto kread = [&](int s, int kb) {
+                const int row = kb * 32 + (lane & 31);
+                const int c = 2 * s + qq;
+                return *reinterpret_cast<const bf16x8 *>(kst + (row * CPR + (c ^ L::fk(row))) * 16);
+            };
+            // K operands are read one k-step ahead of their MFMAs; the
+            // scheduling barriers keep the compiler from hoisting every read
+            // of the tile up front, which would hold 16 operands in registers.
+            bf16x8 kc0 = kread(0, 0), kc1 = kread(0, 1);
 #pragma unroll
-            for (int s = 0; s < KS; ++s)
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    const int row = kb * 32 + (lane & 31);
-                    const int c = 2 * s + qq;
-                    const bf16x8 ka = *reinterpret_cast<const bf16x8 *>(
-                        kst + (row * CPR + (c ^ L::fk(row))) * 16);
-                    sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qb[s], sacc[kb], 0, 0, 0);
+            for (int s = 0; s < KS; ++s) {
+                bf16x8 kn0 = kc0, kn1 = kc1;
+                if (s + 1 < KS) {
+                    kn0 = kread(s + 1, 0);
+                    kn1 = kread(s + 1, 1);
                 }
+                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc0, qb[s], sacc[0], 0, 0, 0);
+                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc1, qb[s], sacc[1], 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+                kc0 = kn0;
+                kc1 = kn1;
+            }
 
             // Mask (diagonal, window-edge and padded-row tiles only) and the
             // row's max.  Lane l holds row r0 + (l & 31) and keys
@@ -302,14 +341,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
                     for (int v = 0; v < 16; ++v)
                         tmax = fmaxf(tmax, sacc[kb][v]);
             } else {
-                const int lo_row = window_lo(my_row, a.window);
-                const bool row_on = my_row <= w_last;
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
-                        const bool keep = row_on && (j <= my_row) && (j >= lo_row);
+                        // lo_row is INT_MAX on inactive rows: nothing kept
+                        const bool keep = (j <= my_pos) && (j >= lo_row);
                         sacc[kb][v] = keep ? sacc[kb][v] : -INFINITY;
                         tmax = fmaxf(tmax, sacc[kb][v]);
                     }
@@ -404,7 +442,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
                 }
                 };
         if (work) {
-            if ((j0 + kPBN - 1 <= r0) && (j0 >= w_lo_last) && (r0 + kPRows - 1 <= w_last))
+            if (w_all && (j0 + kPBN - 1 <= w_first) && (j0 >= w_lo_last))
                 compute(std::true_type{});
             else
                 compute(std::false_type{});
@@ -434,7 +472,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     }
     if (my_row >= a.T)
         return;
-    const bool active = my_row < nb;
+    const bool active = row_on;
     const float inv = (active && lsum > 0.f) ? 1.f / lsum : 0.f;
     uint16_t *orow = a.out + ((int64_t)b * a.T + my_row) * out_stride + (int64_t)h * D;
 #pragma unroll
@@ -498,6 +536,9 @@ hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream) {
     a.v = static_cast<const uint16_t *>(p.v);
     a.out = static_cast<uint16_t *>(p.out);
     a.seqlens = p.seqlens;
+    a.qlens = p.qlens;
+    a.segs = p.segs;
+    a.prefix = p.prefix ? 1 : 0;
     a.records = p.records;
     a.T = p.T; a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
     a.r = p.Hq / p.Hkv;

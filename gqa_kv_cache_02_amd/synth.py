@@ -39,6 +39,17 @@ CONFIGS = {
     "decode_ragged_b32_hq8_hkv2_d64_w4096": dict(kind="decode", dtype="bf16", B=32, Hq=8,
                                                  Hkv=2, d=64, n=(1, 32768), C=32768,
                                                  window=4096, seed=1005),
+    # Queries against a cached prefix: the last 512 cells of a 4096-cell
+    # sequence as new rows (a chunk of a chunked prefill), the prefill shape
+    # above otherwise.
+    "chunk_b1_tq512_c4096_hq32_hkv8_d128": dict(kind="prefix", dtype="bf16", B=1, Tq=512,
+                                                C=4096, Hq=32, Hkv=8, d=128, window=None,
+                                                seed=1006),
+    # The ragged sliding-window decode above over a rolling cache of capacity
+    # w = 4096 (cell j in slot j mod w), with the new cell's key/value
+    # committed in the same call.
+    "ring_b32_hq8_hkv2_d64_w4096": dict(kind="ring", dtype="bf16", B=32, Hq=8, Hkv=2, d=64,
+                                        n=(1, 32768), window=4096, seed=1007),
 }
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}

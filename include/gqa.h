@@ -35,7 +35,7 @@
  *     call never half-advances anything, as the pages require of the cache).
  *   - Preconditions that live in device memory are NOT checked (checking would
  *     need a synchronisation): 0 <= seqlens[b] <= T for prefill and
- *     0 <= seqlens[b] <= C for decode.
+ *     0 <= seqlens[b] <= C for decode (see each entry point for the rest).
  *   - Calls are thread-safe; the library holds no mutable state.
  */
 #ifndef GQA_H
@@ -145,6 +145,83 @@ int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, 
                        const int32_t *seqlens, int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
                        int32_t d, int32_t window, float scale, int32_t dtype, void *workspace,
                        size_t workspace_bytes, int32_t *records, void *stream);
+
+/*
+ * Queries against a cached prefix: chunked prefill, or checking several new
+ * tokens at once, with optional packed segments.
+ * "How do you implement grouped query attention (GQA)?", section "Worked
+ * example" (query i of the t new ones sits at absolute position s - t + i and
+ * sees the keys up to it) and "GQA, FlashAttention and the KV cache",
+ * "The important mask bug with a cache" (several new tokens need that
+ * offset); "Share key/value heads and make context explicit", "Intersect the
+ * window with the context already permitted" (segment starts, intersected
+ * with the window).
+ *
+ *   q          [B, Hq, Tq, d]  the new queries (rows past t_b are padding)
+ *   k_cache    [B, Hkv, C, d]  keys; the caller has already written the new
+ *                              cells, so cells 0..s_b-1 hold the sequence
+ *   v_cache    [B, Hkv, C, d]
+ *   out        [B, Tq, Hq, d]  = merged rows; inactive rows are 0
+ *   seqlens    [B] int32 s_b = cells in the cache including the new ones
+ *              (0 <= s_b <= C), or NULL for s_b = C
+ *   qlens      [B] int32 t_b = new query rows (0 <= t_b <= Tq), or NULL for
+ *              t_b = Tq
+ *   seg_starts [B, Tq] int32: the first cell of each query row's segment
+ *              (packed unrelated examples), or NULL for 0
+ *   records    NULL, or [B, Tq, Hq, 5] index-set records as for
+ *              gqa_prefill_records
+ *   Query row i < t_b sits at cell p = s_b - t_b + i and reads cells lo..p,
+ *   lo = max(seg, p - (w - 1), 0) with a window, lo = seg without.  A row is
+ *   inactive (zero output) when i >= t_b, when p < 0, or when its segment
+ *   starts after it (seg > p).  With qlens == seqlens and no segments this is
+ *   gqa_prefill with cache capacity C; with Tq = 1 it is the decode query.
+ *   Requires 0 <= Tq <= C.  B == 0 or Tq == 0 is a no-op returning GQA_OK.
+ *   Device-side preconditions (not checked): the bounds above on s_b, t_b.
+ */
+int gqa_prefill_prefix(const void *q, const void *k_cache, const void *v_cache, void *out,
+                       const int32_t *seqlens, const int32_t *qlens, const int32_t *seg_starts,
+                       int32_t B, int32_t Tq, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
+                       int32_t window, float scale, int32_t dtype, int32_t *records,
+                       void *stream);
+
+/*
+ * Decode with the new token's key and value committed in the same call,
+ * and/or over a rolling cache.
+ * "Extend the existing full and cached attention paths": the incremental
+ * step reads the candidate key and value at the new position from their own
+ * buffers and commits them to the cache as part of the step.  "Share
+ * key/value heads and make context explicit", the paragraph on the Mistral 7B
+ * report: a rolling buffer that overwrites the oldest entries; with a window
+ * of w cells a buffer of capacity C >= w holds every key the query reads,
+ * cell j in slot j mod C.
+ *
+ *   q        [B, Hq, d]       the new token's queries
+ *   k_cache  [B, Hkv, C, d]   keys (written: the candidate's slot)
+ *   v_cache  [B, Hkv, C, d]   values (written likewise)
+ *   k_new    [B, Hkv, d]      the candidate's key, or NULL (then v_new must
+ *   v_new    [B, Hkv, d]      be NULL too and the cache already holds cell
+ *                             n_b - 1)
+ *   out      [B, Hq, d]
+ *   seqlens  [B] int32 n_b = cells of the sequence including the new one, or
+ *            NULL for n_b = C.  ring == 0: 0 <= n_b <= C, cell j in slot j.
+ *            ring == 1: any n_b >= 0, cell j in slot j mod C; requires
+ *            1 <= window <= C (else GQA_ERR_SHAPE).
+ *   ring     0 or 1 (anything else: GQA_ERR_SHAPE)
+ *   workspace, workspace_bytes: as for gqa_decode, sized by
+ *            gqa_decode_workspace_bytes(B, C, Hq, Hkv, d, window, dtype)
+ *   records  NULL, or [B, Hq, 5] records as for gqa_decode_records (key
+ *            cells, not slots)
+ *   The query sits at cell n_b - 1 and reads cells max(0, n_b - w)..n_b - 1,
+ *   taking cell n_b - 1 from k_new/v_new when they are given; those are also
+ *   copied, bit for bit, into the slot of cell n_b - 1 (n_b == 0 commits
+ *   nothing).  No other cache element changes.  k_new/v_new must not
+ *   overlap the caches.
+ */
+int gqa_decode_cache(const void *q, void *k_cache, void *v_cache, const void *k_new,
+                     const void *v_new, void *out, const int32_t *seqlens, int32_t B, int32_t C,
+                     int32_t Hq, int32_t Hkv, int32_t d, int32_t window, float scale,
+                     int32_t dtype, int32_t ring, void *workspace, size_t workspace_bytes,
+                     int32_t *records, void *stream);
 
 /* The kernel family gqa_prefill / gqa_decode would launch for these arguments
  * (GQA_KERNEL_NONE for a no-op or a refused call).  Alignment is assumed. */

@@ -148,3 +148,51 @@ def test_workspace_size_and_kernel_choice():
     # a window bounds the work, so it can only shrink the workspace
     assert (L.gqa_decode_workspace_bytes(32, 32768, 8, 2, 64, 4096, 1)
             <= L.gqa_decode_workspace_bytes(32, 32768, 8, 2, 64, -1, 1))
+
+
+def _prefix(**kw):
+    a = dict(q=P, k=P, v=P, out=P, seqlens=None, qlens=None, segs=None, B=1, Tq=4, C=8, Hq=4,
+             Hkv=2, d=8, window=-1, scale=0.5, dtype=0, rec=None)
+    a.update(kw)
+    return gqa.lib().gqa_prefill_prefix(a["q"], a["k"], a["v"], a["out"], a["seqlens"],
+                                        a["qlens"], a["segs"], a["B"], a["Tq"], a["C"], a["Hq"],
+                                        a["Hkv"], a["d"], a["window"], a["scale"], a["dtype"],
+                                        a["rec"], None)
+
+
+def _dcache(**kw):
+    a = dict(q=P, k=P, v=P, kn=None, vn=None, out=P, seqlens=None, B=2, C=64, Hq=8, Hkv=2,
+             d=128, window=16, scale=0.5, dtype=1, ring=1, ws=P, wsb=1 << 30, rec=None)
+    a.update(kw)
+    return gqa.lib().gqa_decode_cache(a["q"], a["k"], a["v"], a["kn"], a["vn"], a["out"],
+                                      a["seqlens"], a["B"], a["C"], a["Hq"], a["Hkv"], a["d"],
+                                      a["window"], a["scale"], a["dtype"], a["ring"], a["ws"],
+                                      a["wsb"], a["rec"], None)
+
+
+def test_refusals_prefill_prefix():
+    assert _prefix(Hq=6, Hkv=4) == HEADS
+    assert _prefix(window=0) == ZERO_WINDOW
+    assert _prefix(Tq=9, C=8) == SHAPE          # more query rows than cells
+    assert _prefix(q=None) == NULL
+    assert _prefix(qlens=ctypes.c_void_p(4098)) == ALIGN
+    assert _prefix(segs=ctypes.c_void_p(4098)) == ALIGN
+    assert _prefix(rec=ctypes.c_void_p(4098)) == ALIGN
+    assert _prefix(B=0, q=None, k=None, v=None, out=None) == OK
+    assert _prefix(Tq=0, q=None, k=None, v=None, out=None) == OK
+
+
+def test_refusals_decode_cache():
+    assert _dcache(ring=2) == SHAPE
+    assert _dcache(window=-1) == SHAPE           # a rolling cache needs a window
+    assert _dcache(window=65) == SHAPE           # ... no longer than the capacity
+    assert _dcache(window=0) == ZERO_WINDOW
+    assert _dcache(kn=P) == NULL                 # the key without the value
+    assert _dcache(vn=P) == NULL
+    assert _dcache(kn=P_ODD, vn=P) == ALIGN
+    assert _dcache(ring=0, window=-1, wsb=0) == WORKSPACE
+    assert _dcache(B=0, q=None, k=None, v=None, out=None) == OK
+    # a rolling cache sizes its workspace from the window, like gqa_decode
+    L = gqa.lib()
+    need = L.gqa_decode_workspace_bytes(2, 64, 8, 2, 128, 16, 1)
+    assert _dcache(wsb=need - 1) == WORKSPACE
