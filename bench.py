@@ -23,6 +23,13 @@ Prints ONE JSON line.
   prefill        causal prefill B=1, T=4096, Hq=32, Hkv=8, d=128: TFLOP/s of
                  the permitted pairs (4*d flops each) against 2.5 PFLOP/s
                  dense bf16 MFMA.
+  prefix_prefill queries against a cached prefix: the last 512 cells of a
+                 4096-cell sequence as new rows (B=1, Hq=32, Hkv=8, d=128):
+                 TFLOP/s of the permitted pairs against 2.5 PFLOP/s.
+  ring_decode    decode over a rolling cache of capacity w = 4096 with the new
+                 cell committed in the call (B=32, Hq=8, Hkv=2, d=64, ragged
+                 lengths in [1, 32768]): GB/s of the K/V cells in each row's
+                 window read once per KV group, against 8 TB/s.
   cpu_baseline   the fp64 oracle (plain C, OpenMP) on the host cores, on the
                  same decode workload.
 """
@@ -153,6 +160,78 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
                 timing="HIP events on the launch stream around each call")
 
 
+def _time_calls(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    for i in range(steps):
+        ev[2 * i].record()
+        fn(i)
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+    return sum(per) / steps
+
+
+def prefix_flops(Hq, d, C, Tq, B=1):
+    """4*d flops per permitted pair; row i of the Tq new ones at cell
+    C - Tq + i reads C - Tq + i + 1 keys."""
+    pairs = Tq * (C - Tq) + Tq * (Tq + 1) // 2
+    return 4 * Hq * d * B * pairs
+
+
+def bench_prefix(torch, gqa, synth, steps, warmup):
+    cfg = synth.CONFIGS["chunk_b1_tq512_c4096_hq32_hkv8_d128"]
+    B, Tq, C, hq, hkv, d = cfg["B"], cfg["Tq"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    dev = torch.device("cuda:0")
+    q, k, v = synth.prefill_inputs(B, Tq, hq, hkv, d, torch.bfloat16, cfg["seed"], dev, C=C)
+    out = torch.empty((B, Tq, hq, d), dtype=torch.bfloat16, device=dev)
+    ms = _time_calls(torch, lambda i: gqa.prefill_prefix(q, k, v, out=out), steps, warmup)
+    flops = prefix_flops(hq, d, C, Tq, B)
+    tflops = flops / (ms * 1e-3) / 1e12
+    return dict(workload="gqa_prefill_prefix_b1_tq512_c4096_hq32_hkv8_d128_bf16",
+                ms=round(ms, 5), flops=flops, tflops=round(tflops, 2),
+                frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
+                tokens_per_s=round(B * Tq / (ms * 1e-3), 1),
+                timing="HIP events on the launch stream around each call")
+
+
+def bench_ring(torch, gqa, synth, steps, warmup):
+    cfg = synth.CONFIGS["ring_b32_hq8_hkv2_d64_w4096"]
+    B, hq, hkv, d, w = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["window"]
+    lo, hi = cfg["n"]
+    dev = torch.device("cuda:0")
+    lens = synth.ragged_lengths(B, lo, hi, cfg["seed"])
+    seqlens = lens.to(dev)
+    # 6 rotated copies of the 67 MB rolling cache keep it out of the 256 MB
+    # Infinity Cache between steps
+    copies = 6
+    q, k0, v0 = synth.decode_inputs(B, w, hq, hkv, d, torch.bfloat16, cfg["seed"], dev)
+    ks, vs = [k0], [v0]
+    for i in range(1, copies):
+        _, k, v = synth.decode_inputs(B, w, hq, hkv, d, torch.bfloat16, cfg["seed"] + 100 * i, dev)
+        ks.append(k)
+        vs.append(v)
+    kn = synth.randn((B, hkv, d), cfg["seed"] + 50, torch.bfloat16, dev)
+    vn = synth.randn((B, hkv, d), cfg["seed"] + 51, torch.bfloat16, dev)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, w, hq, hkv, d, w)), dtype=torch.uint8,
+                     device=dev)
+    ms = _time_calls(torch, lambda i: gqa.decode_cache(q, ks[i % copies], vs[i % copies],
+                                                       k_new=kn, v_new=vn, seqlens=seqlens,
+                                                       window=w, ring=True, out=out,
+                                                       workspace=ws), steps, warmup)
+    cells = int(sum(min(int(n), w) for n in lens.tolist()))
+    nbytes = 2 * hkv * cells * d * 2 + 2 * B * hq * d * 2 + 4 * B * hkv * d * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload="gqa_decode_cache_ring_b32_hq8_hkv2_d64_w4096_bf16",
+                ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
+                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
+                timing="HIP events on the launch stream around each call")
+
+
 def copy_calibration(torch):
     """A plain device copy of COPY_CAL_BYTES, so that rocprofv3's FETCH_SIZE
     and WRITE_SIZE counters can be scaled against a known transfer."""
@@ -264,6 +343,8 @@ def main():
     line["roofline"]["hbm_copy_reference_gbs"] = hbm_copy_reference(torch)
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3)
+        line["prefix_prefill"] = bench_prefix(torch, gqa, synth, max(10, args.steps // 10), 3)
+    line["ring_decode"] = bench_ring(torch, gqa, synth, max(20, args.steps // 2), 10)
     if args.copy_calibration:
         copy_calibration(torch)
         line["copy_calibration_bytes"] = COPY_CAL_BYTES
