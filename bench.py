@@ -187,7 +187,10 @@ def bench_prefix(torch, gqa, synth, steps, warmup):
     dev = torch.device("cuda:0")
     q, k, v = synth.prefill_inputs(B, Tq, hq, hkv, d, torch.bfloat16, cfg["seed"], dev, C=C)
     out = torch.empty((B, Tq, hq, d), dtype=torch.bfloat16, device=dev)
-    ms = _time_calls(torch, lambda i: gqa.prefill_prefix(q, k, v, out=out), steps, warmup)
+    ws = torch.empty(max(1, gqa.prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d)),
+                     dtype=torch.uint8, device=dev)
+    ms = _time_calls(torch, lambda i: gqa.prefill_prefix(q, k, v, out=out, workspace=ws),
+                     steps, warmup)
     flops = prefix_flops(hq, d, C, Tq, B)
     tflops = flops / (ms * 1e-3) / 1e12
     return dict(workload="gqa_prefill_prefix_b1_tq512_c4096_hq32_hkv8_d128_bf16",

@@ -66,7 +66,9 @@ def _load():
     L.gqa_decode.restype = ctypes.c_int
     L.gqa_decode_records.argtypes = [vp] * 5 + [i32] * 6 + [f32, i32, vp, sz, vp, vp]
     L.gqa_decode_records.restype = ctypes.c_int
-    L.gqa_prefill_prefix.argtypes = [vp] * 7 + [i32] * 7 + [f32, i32, vp, vp]
+    L.gqa_prefill_prefix.argtypes = [vp] * 7 + [i32] * 7 + [f32, i32, vp, sz, vp, vp]
+    L.gqa_prefill_prefix_workspace_bytes.argtypes = [i32] * 8
+    L.gqa_prefill_prefix_workspace_bytes.restype = sz
     L.gqa_prefill_prefix.restype = ctypes.c_int
     L.gqa_decode_cache.argtypes = [vp] * 7 + [i32] * 6 + [f32, i32, i32, vp, sz, vp, vp]
     L.gqa_decode_cache.restype = ctypes.c_int
@@ -261,8 +263,14 @@ def _rowmeta(name, t, shape, device):
     return t
 
 
+def prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, window=None,
+                                   dtype=torch.bfloat16) -> int:
+    return int(_load().gqa_prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, _win(window),
+                                                          _dt(dtype)))
+
+
 def prefill_prefix(q, k, v, *, seqlens=None, qlens=None, seg_starts=None, window=None,
-                   scale=None, out=None, records=None):
+                   scale=None, out=None, workspace=None, records=None):
     """Queries against a cached prefix (chunked prefill / several new tokens),
     optionally with packed segments.  q [B,Hq,Tq,d], k/v [B,Hkv,C,d] ->
     out [B,Tq,Hq,d].  Query row i of the t_b = qlens[b] new ones sits at cell
@@ -290,9 +298,14 @@ def prefill_prefix(q, k, v, *, seqlens=None, qlens=None, seg_starts=None, window
         if records.shape != (B, Tq, hq, 5):
             raise ValueError("records must be int32 [B,Tq,Hq,5]")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = int(L.gqa_prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, _win(window),
+                                                    _dt(q.dtype)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_tensor("workspace", workspace, torch.uint8, dev)
     rc = L.gqa_prefill_prefix(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sl), _ptr(ql),
                               _ptr(sg), B, Tq, C, hq, hkv, d, _win(window), sc, _dt(q.dtype),
-                              _ptr(records), _stream(dev))
+                              _ptr(workspace), workspace.numel(), _ptr(records), _stream(dev))
     if rc:
         raise GQAError(rc, "gqa_prefill_prefix")
     return out

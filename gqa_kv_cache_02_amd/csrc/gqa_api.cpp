@@ -95,6 +95,8 @@ struct PrefixExtra {
     bool prefix = false;
     const int32_t *qlens = nullptr;
     const int32_t *segs = nullptr;
+    void *workspace = nullptr; // key-range split partials (prefix form only)
+    size_t workspace_bytes = 0;
 };
 struct CacheExtra {
     const void *knew = nullptr;
@@ -135,9 +137,21 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
     p.segs = x.segs;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (prefill_kernel_for(d, dtype) == GQA_KERNEL_PREFILL_MFMA && fast_aligned(q, k, v, out)) {
-        if (!gqa::prefill_grid_ok(B, T, Hq, Hkv))
+        gqa::PrefixPlan plan{};
+        plan.nsplit = 1;
+        if (x.prefix)
+            plan = gqa::plan_prefix(B, T, C, Hq, Hkv, d, window);
+        if (!gqa::prefill_grid_ok(B, T, Hq, Hkv, plan.nsplit))
             return GQA_ERR_SHAPE;
-        return status_of(gqa::launch_prefill_mfma(p, s));
+        if (plan.nsplit > 1) {
+            if (!x.workspace)
+                return GQA_ERR_NULL;
+            if (!aligned(x.workspace, 256))
+                return GQA_ERR_ALIGN;
+            if (x.workspace_bytes < plan.bytes)
+                return GQA_ERR_WORKSPACE;
+        }
+        return status_of(gqa::launch_prefill_mfma(p, plan, x.workspace, s));
     }
     if (B > kMaxGridYZ || (int64_t)Hkv * ((r + 7) / 8) > kMaxGridYZ)
         return GQA_ERR_SHAPE;
@@ -248,15 +262,29 @@ int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, 
                        workspace, workspace_bytes, records, true, stream);
 }
 
+size_t gqa_prefill_prefix_workspace_bytes(int32_t B, int32_t Tq, int32_t C, int32_t Hq,
+                                          int32_t Hkv, int32_t d, int32_t window,
+                                          int32_t dtype) {
+    if (check_scalars(Hq, Hkv, d, window, 1.0f, dtype) || B < 0 || Tq < 0 || C < 0 || Tq > C ||
+        check_sizes(B, Hq, Hkv, Tq, C, d, dtype))
+        return 0;
+    if (B == 0 || Tq == 0 || prefill_kernel_for(d, dtype) != GQA_KERNEL_PREFILL_MFMA)
+        return 0;
+    const gqa::PrefixPlan plan = gqa::plan_prefix(B, Tq, C, Hq, Hkv, d, window);
+    return plan.nsplit > 1 ? plan.bytes : 0;
+}
+
 int gqa_prefill_prefix(const void *q, const void *k_cache, const void *v_cache, void *out,
                        const int32_t *seqlens, const int32_t *qlens, const int32_t *seg_starts,
                        int32_t B, int32_t Tq, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
-                       int32_t window, float scale, int32_t dtype, int32_t *records,
-                       void *stream) {
+                       int32_t window, float scale, int32_t dtype, void *workspace,
+                       size_t workspace_bytes, int32_t *records, void *stream) {
     PrefixExtra x;
     x.prefix = true;
     x.qlens = qlens;
     x.segs = seg_starts;
+    x.workspace = workspace;
+    x.workspace_bytes = workspace_bytes;
     return prefill_impl(q, k_cache, v_cache, out, seqlens, B, Tq, C, Hq, Hkv, d, window, scale,
                         dtype, records, records != nullptr, stream, x);
 }

@@ -61,7 +61,20 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window);
 hipError_t launch_generic(const Problem &p, hipStream_t stream);
 hipError_t launch_decode_split(const Problem &p, const DecodePlan &plan, void *workspace,
                                hipStream_t stream);
-hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream);
-bool prefill_grid_ok(int B, int T, int Hq, int Hkv);
+// Key-range split of the MFMA prefill for queries against a cached prefix:
+// nsplit parts of tps tiles; workspace layout: normalised partial outputs
+// [nsplit, B, T, Hq, d] fp32, their log2-sum-exp [nsplit, B, T, Hq] fp32 and
+// index-set partials [nsplit, B, T, Hq, 4] int32 (each 256-byte aligned).
+// nsplit == 1: no split, no workspace.
+struct PrefixPlan {
+    int nsplit;
+    int tps;
+    size_t o_off, lse_off, rec_off, bytes;
+};
+PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window);
+
+hipError_t launch_prefill_mfma(const Problem &p, const PrefixPlan &plan, void *workspace,
+                               hipStream_t stream);
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit);
 
 } // namespace gqa

@@ -25,6 +25,7 @@
 // window with the context already permitted").
 #include <limits.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "gqa_common.hpp"
@@ -48,6 +49,12 @@ struct PrefillArgs {
     int32_t *records;
     int B, T, C, Hq, Hkv, window, r, hpw, rb, nhc, nqb;
     int prefix;             // query rows sit at s_b - t_b + i (else at i, t_b = s_b = n_b)
+    // Split of each block's key range over nsplit workgroups of tps tiles
+    // (nsplit > 1: partials to the workspace, merged by prefix_merge_kernel).
+    int nsplit, tps;
+    float *o_part;          // [nsplit, B, T, Hq, D] normalised partial outputs
+    float *lse_part;        // [nsplit, B, T, Hq] log2-sum-exp (-inf: no key)
+    int32_t *rec_part;      // [nsplit, B, T, Hq, 4] {count, lowest, highest, xor}
     float scale_log2; // |scale| * log2(e)
     uint32_t qneg;    // 0x80008000 when scale < 0: Q's sign bits are flipped on load
 };
@@ -122,9 +129,12 @@ void prefill_mfma_kernel(PrefillArgs a) {
     // indices differ in (batch row, KV group, head chunk); with 8 or a
     // multiple of them per query block, each XCD keeps seeing the same KV
     // groups, whose K/V then stay in that XCD's L2.
+    // (With a split key range the split index sits between the query block
+    // and the (b, g, head chunk) index.)
     const int per_blk = a.B * a.Hkv * a.nhc;
     const int lin_id = static_cast<int>(blockIdx.x);
-    const int qblk = a.nqb - 1 - lin_id / per_blk; // heaviest blocks first
+    const int qblk = a.nqb - 1 - lin_id / (per_blk * a.nsplit); // heaviest blocks first
+    const int split = (lin_id / per_blk) % a.nsplit;
     const int rest = lin_id % per_blk;
     const int b = rest / (a.Hkv * a.nhc);
     const int g = (rest / a.nhc) % a.Hkv;
@@ -179,6 +189,44 @@ void prefill_mfma_kernel(PrefillArgs a) {
     }
     const int64_t out_stride = (int64_t)a.Hq * D; // between cells in [B,T,Hq,D]
 
+    // This workgroup's tiles: the block's key range, or its split-th part.
+    int tile_lo = wg_lo / kPBN;
+    int tile_hi = wg_last / kPBN;
+    if (a.nsplit > 1) {
+        tile_lo += split * a.tps;
+        tile_hi = min(tile_hi, tile_lo + a.tps - 1);
+    }
+    // Partial results of a split key range: this split's normalised output,
+    // its log2-sum-exp (-inf when it folded no key) and its index-set part.
+    auto write_part = [&](int row, const float *o4, float lse, int cnt, int klo, int khi, int kx,
+                          bool with_o) {
+        const int64_t prow = (((int64_t)split * a.B + b) * a.T + row) * a.Hq + h;
+        if (with_o) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v4 = 0; v4 < 4; ++v4) {
+                    const int col = db * 32 + 8 * v4 + 4 * (lane >> 5);
+                    *reinterpret_cast<float4 *>(a.o_part + prow * D + col) =
+                        make_float4(o4[(db * 4 + v4) * 4 + 0], o4[(db * 4 + v4) * 4 + 1],
+                                    o4[(db * 4 + v4) * 4 + 2], o4[(db * 4 + v4) * 4 + 3]);
+                }
+        }
+        if ((lane >> 5) == 0) {
+            a.lse_part[prow] = lse;
+            if (kRecord) {
+                int32_t *rp = a.rec_part + prow * 4;
+                rp[0] = cnt; rp[1] = klo; rp[2] = khi; rp[3] = kx;
+            }
+        }
+    };
+
+    if (a.nsplit > 1 && (wg_last < 0 || tile_lo > tile_hi)) {
+        // nothing to fold in this split: an empty partial for every row
+        if (wave_on && (lane >> 5) == 0 && my_row < a.T)
+            write_part(my_row, nullptr, -INFINITY, 0, INT_MAX, -1, 0, false);
+        return;
+    }
     if (wg_last < 0) {
         // no active row: the whole block is padding, write zeros
         if (wave_on) {
@@ -197,8 +245,6 @@ void prefill_mfma_kernel(PrefillArgs a) {
         }
         return;
     }
-    const int tile_lo = wg_lo / kPBN;
-    const int tile_hi = wg_last / kPBN;
 
     // Q^T operand, kept for the whole loop: lane l holds row r0 + (l & 31),
     // features s*16 + 8*(l >> 5) .. +8 (sign bits flipped for a negative scale).
@@ -474,6 +520,18 @@ void prefill_mfma_kernel(PrefillArgs a) {
         return;
     const bool active = row_on;
     const float inv = (active && lsum > 0.f) ? 1.f / lsum : 0.f;
+    if (a.nsplit > 1) {
+        float o4[DB * 16];
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                o4[db * 16 + e] = oacc[db][e] * inv;
+        const bool folded = active && lsum > 0.f;
+        write_part(my_row, o4, folded ? m + __builtin_amdgcn_logf(lsum) : -INFINITY,
+                   folded ? r_cnt : 0, r_lo, r_hi, r_xor, true);
+        return;
+    }
     uint16_t *orow = a.out + ((int64_t)b * a.T + my_row) * out_stride + (int64_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -490,6 +548,64 @@ void prefill_mfma_kernel(PrefillArgs a) {
         rec[0] = g;
         if (active) {
             rec[1] = r_lo; rec[2] = r_hi; rec[3] = r_cnt; rec[4] = r_xor;
+        } else {
+            rec[1] = -1; rec[2] = -1; rec[3] = 0; rec[4] = 0;
+        }
+    }
+}
+
+// Merge of a split key range: one thread per 4 output features of a row
+// (b, i, h); out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse)
+// ("GQA, FlashAttention and the KV cache", section "FlashAttention").  A row
+// no split folded a key into is inactive: zero output.
+template <int D, bool kRecord>
+__global__ __launch_bounds__(256) void prefix_merge_kernel(PrefillArgs a) {
+    constexpr int Q4 = D / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t rows = (int64_t)a.B * a.T * a.Hq;
+    if (idx >= rows * Q4)
+        return;
+    const int64_t row = idx / Q4; // (b * T + i) * Hq + h
+    const int c4 = static_cast<int>(idx % Q4) * 4;
+    float mx = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s)
+        mx = fmaxf(mx, a.lse_part[s * rows + row]);
+    uint2 pk = uint2{0u, 0u};
+    if (mx != -INFINITY) {
+        float den = 0.f;
+        float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int s = 0; s < a.nsplit; ++s) {
+            const float l = a.lse_part[s * rows + row];
+            if (l == -INFINITY)
+                continue; // nothing folded (its partial output was never written)
+            const float w = fast_exp2(l - mx);
+            const float4 o = *reinterpret_cast<const float4 *>(a.o_part + (s * rows + row) * D + c4);
+            den += w;
+            acc.x = fmaf(w, o.x, acc.x);
+            acc.y = fmaf(w, o.y, acc.y);
+            acc.z = fmaf(w, o.z, acc.z);
+            acc.w = fmaf(w, o.w, acc.w);
+        }
+        const float inv = 1.f / den;
+        pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
+        pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
+    }
+    *reinterpret_cast<uint2 *>(a.out + row * D + c4) = pk;
+    if (kRecord && c4 == 0) {
+        int cnt = 0, x = 0, rl = INT_MAX, rh = -1;
+        for (int s = 0; s < a.nsplit; ++s) {
+            const int32_t *rp = a.rec_part + (s * rows + row) * 4;
+            if (a.lse_part[s * rows + row] == -INFINITY)
+                continue;
+            cnt += rp[0];
+            rl = min(rl, rp[1]);
+            rh = max(rh, rp[2]);
+            x ^= rp[3];
+        }
+        int32_t *rec = a.records + row * 5;
+        rec[0] = static_cast<int>(row % a.Hq) / a.r;
+        if (cnt > 0) {
+            rec[1] = rl; rec[2] = rh; rec[3] = cnt; rec[4] = x;
         } else {
             rec[1] = -1; rec[2] = -1; rec[3] = 0; rec[4] = 0;
         }
@@ -518,18 +634,63 @@ static int64_t prefill_workgroups(int B, int T, int Hq, int Hkv) {
     return nqb * B * Hkv * ((Hq / Hkv) / hpw);
 }
 
-bool prefill_grid_ok(int B, int T, int Hq, int Hkv) {
-    const int64_t wgs = prefill_workgroups(B, T, Hq, Hkv);
-    return T >= 0 && wgs * 256 <= (int64_t)UINT32_MAX;
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit) {
+    const int64_t wgs = prefill_workgroups(B, T, Hq, Hkv) * (nsplit > 1 ? nsplit : 1);
+    return T >= 0 && wgs * 256 <= (int64_t)UINT32_MAX &&
+           (int64_t)B * T * Hq * 64 <= (int64_t)UINT32_MAX; // merge grid
+}
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Split of the key range for queries against a cached prefix: when the
+// blocks alone give fewer than 512 workgroups (two per CU on 256 CUs), each
+// block's key range is cut into nsplit parts of tps tiles (at least 4).  The
+// plan depends only on the arguments (the workspace size is a function of
+// them).
+PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window) {
+    PrefixPlan p{};
+    p.nsplit = 1;
+    p.tps = 0;
+    int hpw, rb;
+    prefill_shape(Hq / Hkv, &hpw, &rb);
+    const int64_t nqb = ((int64_t)T + kPRows * rb - 1) / (kPRows * rb);
+    const int64_t units = nqb * B * Hkv * ((Hq / Hkv) / hpw);
+    const int64_t elig = (window > 0 && window < C) ? window : C;
+    // tiles a block can span: its rows' key ranges, at most the cache
+    const int64_t maxtiles = std::min<int64_t>((C + kPBN - 1) / kPBN,
+                                               (elig + kPRows * rb) / kPBN + 2);
+    const int64_t target = 512;
+    if (units > 0 && units < target && maxtiles >= 8) {
+        int64_t ns = (target + units - 1) / units;
+        ns = std::min<int64_t>(ns, maxtiles / 4);
+        if (ns > 1) {
+            p.tps = static_cast<int>((maxtiles + ns - 1) / ns);
+            p.nsplit = static_cast<int>((maxtiles + p.tps - 1) / p.tps);
+        }
+    }
+    if (p.nsplit > 1) {
+        const size_t rows = (size_t)p.nsplit * B * T * Hq;
+        p.o_off = 0;
+        p.lse_off = align256(rows * d * sizeof(float));
+        p.rec_off = p.lse_off + align256(rows * sizeof(float));
+        p.bytes = p.rec_off + align256(rows * 4 * sizeof(int32_t));
+    }
+    return p;
 }
 
 template <int D, bool kRecord>
 static hipError_t launch_p(const PrefillArgs &a, dim3 grid, hipStream_t s) {
     prefill_mfma_kernel<D, kRecord><<<grid, 256, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit <= 1)
+        return e;
+    const int64_t threads = (int64_t)a.B * a.T * a.Hq * (D / 4);
+    prefix_merge_kernel<D, kRecord><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream) {
+hipError_t launch_prefill_mfma(const Problem &p, const PrefixPlan &plan, void *workspace,
+                               hipStream_t stream) {
     PrefillArgs a;
     a.q = static_cast<const uint16_t *>(p.q);
     a.k = static_cast<const uint16_t *>(p.k);
@@ -548,7 +709,13 @@ hipError_t launch_prefill_mfma(const Problem &p, hipStream_t stream) {
     a.scale_log2 = fabsf(p.scale) * kLog2e;
     a.qneg = p.scale < 0.f ? 0x80008000u : 0u;
     a.B = p.B;
-    dim3 grid(static_cast<uint32_t>(prefill_workgroups(p.B, p.T, p.Hq, p.Hkv)), 1, 1);
+    a.nsplit = plan.nsplit > 1 ? plan.nsplit : 1;
+    a.tps = plan.tps;
+    unsigned char *w = static_cast<unsigned char *>(workspace);
+    a.o_part = a.nsplit > 1 ? reinterpret_cast<float *>(w + plan.o_off) : nullptr;
+    a.lse_part = a.nsplit > 1 ? reinterpret_cast<float *>(w + plan.lse_off) : nullptr;
+    a.rec_part = a.nsplit > 1 ? reinterpret_cast<int32_t *>(w + plan.rec_off) : nullptr;
+    dim3 grid(static_cast<uint32_t>(prefill_workgroups(p.B, p.T, p.Hq, p.Hkv) * a.nsplit), 1, 1);
     const bool rec = p.records != nullptr;
     if (p.d == 128)
         return rec ? launch_p<128, true>(a, grid, stream) : launch_p<128, false>(a, grid, stream);

@@ -168,6 +168,12 @@ int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, 
  *              t_b = Tq
  *   seg_starts [B, Tq] int32: the first cell of each query row's segment
  *              (packed unrelated examples), or NULL for 0
+ *   workspace  device scratch of at least gqa_prefill_prefix_workspace_bytes(...)
+ *              bytes, 256-byte aligned (may be NULL when that size is 0).  When
+ *              the blocks of new rows alone cannot fill the GPU, their key
+ *              ranges are split over several workgroups whose partial results
+ *              go here and are merged by a second kernel.  Contents on entry
+ *              do not matter; calls that may overlap must not share it.
  *   records    NULL, or [B, Tq, Hq, 5] index-set records as for
  *              gqa_prefill_records
  *   Query row i < t_b sits at cell p = s_b - t_b + i and reads cells lo..p,
@@ -178,11 +184,14 @@ int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, 
  *   Requires 0 <= Tq <= C.  B == 0 or Tq == 0 is a no-op returning GQA_OK.
  *   Device-side preconditions (not checked): the bounds above on s_b, t_b.
  */
+size_t gqa_prefill_prefix_workspace_bytes(int32_t B, int32_t Tq, int32_t C, int32_t Hq,
+                                          int32_t Hkv, int32_t d, int32_t window,
+                                          int32_t dtype);
 int gqa_prefill_prefix(const void *q, const void *k_cache, const void *v_cache, void *out,
                        const int32_t *seqlens, const int32_t *qlens, const int32_t *seg_starts,
                        int32_t B, int32_t Tq, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
-                       int32_t window, float scale, int32_t dtype, int32_t *records,
-                       void *stream);
+                       int32_t window, float scale, int32_t dtype, void *workspace,
+                       size_t workspace_bytes, int32_t *records, void *stream);
 
 /*
  * Decode with the new token's key and value committed in the same call,

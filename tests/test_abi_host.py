@@ -152,12 +152,12 @@ def test_workspace_size_and_kernel_choice():
 
 def _prefix(**kw):
     a = dict(q=P, k=P, v=P, out=P, seqlens=None, qlens=None, segs=None, B=1, Tq=4, C=8, Hq=4,
-             Hkv=2, d=8, window=-1, scale=0.5, dtype=0, rec=None)
+             Hkv=2, d=8, window=-1, scale=0.5, dtype=0, ws=None, wsb=0, rec=None)
     a.update(kw)
     return gqa.lib().gqa_prefill_prefix(a["q"], a["k"], a["v"], a["out"], a["seqlens"],
                                         a["qlens"], a["segs"], a["B"], a["Tq"], a["C"], a["Hq"],
                                         a["Hkv"], a["d"], a["window"], a["scale"], a["dtype"],
-                                        a["rec"], None)
+                                        a["ws"], a["wsb"], a["rec"], None)
 
 
 def _dcache(**kw):
@@ -180,6 +180,16 @@ def test_refusals_prefill_prefix():
     assert _prefix(rec=ctypes.c_void_p(4098)) == ALIGN
     assert _prefix(B=0, q=None, k=None, v=None, out=None) == OK
     assert _prefix(Tq=0, q=None, k=None, v=None, out=None) == OK
+    # few new rows against a long cache split the key range and need a workspace
+    L = gqa.lib()
+    need = L.gqa_prefill_prefix_workspace_bytes(1, 512, 4096, 32, 8, 128, -1, 1)
+    assert need > 0
+    assert L.gqa_prefill_prefix_workspace_bytes(1, 4096, 4096, 32, 8, 128, -1, 1) == 0
+    assert L.gqa_prefill_prefix_workspace_bytes(1, 512, 4096, 32, 8, 128, -1, 0) == 0  # fp32
+    big = dict(B=1, Tq=512, C=4096, Hq=32, Hkv=8, d=128, dtype=1)
+    assert _prefix(**big, ws=None, wsb=0) == NULL
+    assert _prefix(**big, ws=P, wsb=need - 1) == WORKSPACE
+    assert _prefix(**big, ws=ctypes.c_void_p(4096 + 16), wsb=need) == ALIGN
 
 
 def test_refusals_decode_cache():

@@ -110,6 +110,22 @@ def test_prefix_one_token_matches_decode():
         assert _maxerr(_np(a)[:, 0], _np(b)) <= BF16_TOL
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefix_split_key_range(d):
+    # few new rows against long caches: the key range of every block is split
+    # over several workgroups and merged; ragged lengths leave whole splits
+    # empty, rows before cell 0 and windows leave rows with no key in a split
+    B, Tq, C = 2, 64, 2000
+    for hq, hkv in ((8, 2), (4, 4), (6, 2)):
+        q, k, v = synth.prefill_inputs(B, Tq, hq, hkv, d, torch.bfloat16, 3150 + d + hq, DEV, C=C)
+        for w in (None, 1000, 64):
+            assert gqa.prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, w) > 0 or w == 64
+            for seqlens, qlens in (([2000, 1500], [64, 64]), ([2000, 40], [1, 64]), (None, None)):
+                check_prefix(q, k, v, seqlens, qlens, None, w, ("split", hq, hkv))
+        segs = _packed_segments(B, Tq, 3160 + d, 30) + 1900
+        check_prefix(q, k, v, [2000, 2000], [64, 64], segs, None, ("split+segments", hq, hkv))
+
+
 # ---------------------------------------------------------------------------
 # packed segments
 # ---------------------------------------------------------------------------
