@@ -459,20 +459,25 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
         return; // finished by the split kernel
     const float *lse = a.lse_part + row * a.nsplit;
     const float *op = a.o_part + row * a.nsplit * D + c4;
+    // One pass with a running maximum: no load depends on another, so the
+    // partials of every chunk are in flight together.  Every chunk of a row
+    // with ns > 1 folded at least one key, so each lse_s is finite.
     float mx = -INFINITY;
-    for (int s = 0; s < ns; ++s)
-        mx = fmaxf(mx, lse[s]);
     float den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 4
+#pragma unroll 8
     for (int s = 0; s < ns; ++s) {
-        const float w = fast_exp2(lse[s] - mx);
+        const float l = lse[s];
         const float4 o = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
-        den += w;
-        acc.x = fmaf(w, o.x, acc.x);
-        acc.y = fmaf(w, o.y, acc.y);
-        acc.z = fmaf(w, o.z, acc.z);
-        acc.w = fmaf(w, o.w, acc.w);
+        const float mn = fmaxf(mx, l);
+        const float sc = fast_exp2(mx - mn); // 0 on the first chunk (mx = -inf)
+        const float w = fast_exp2(l - mn);
+        den = fmaf(den, sc, w);
+        acc.x = fmaf(acc.x, sc, w * o.x);
+        acc.y = fmaf(acc.y, sc, w * o.y);
+        acc.z = fmaf(acc.z, sc, w * o.z);
+        acc.w = fmaf(acc.w, sc, w * o.w);
+        mx = mn;
     }
     const float inv = 1.f / den;
     uint2 pk;
