@@ -43,6 +43,8 @@
 // make context explicit"), with a window of at most C cells.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "gqa_common.hpp"
 #include "gqa_internal.hpp"
 
@@ -138,13 +140,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // Q^T operand: lane (hl, qg) holds features s*32 + qg*8 .. +8 of head hl.
     bf16x8 qb[KS];
     {
-        const uint16_t *qrow = a.q + (row0 + hl) * D;
+        // columns past the group's last head read that head and are zeroed
+        const uint16_t *qrow = a.q + (row0 + min(hl, nh - 1)) * D;
+        const bf16x8 zero = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            if (hl < nh)
-                qb[s] = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + qg * 8);
-            else
-                qb[s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            const bf16x8 t = *reinterpret_cast<const bf16x8 *>(qrow + s * 32 + qg * 8);
+            qb[s] = (hl < nh) ? t : zero;
         }
     }
 
@@ -193,37 +195,31 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // One tile's loads: K in the MFMA operand layout (lane (hl, qg) of key
     // block kb holds key j0 + kb*16 + hl, features s*32 + qg*8 .. +8) and V in
-    // its natural layout (16 B per lane, 1 KiB per load).  Cells past the
-    // chunk end are zero-filled and never read.
+    // its natural layout (16 B per lane, 1 KiB per load).  Keys past the chunk
+    // end re-read the chunk's last cell instead of branching around the load:
+    // their scores are masked to -inf and their values get weight 0, and that
+    // cell is permitted, so its values are the caller's data.
     auto load_tile = [&](int j0, bf16x8 (&ka)[2][KS], u32x4 (&vr)[VIT]) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            const int key = j0 + kb * 16 + hl;
+            const int key = min(j0 + kb * 16 + hl, c_hi);
             const uint16_t *krow = kbase + cell(key) * D + qg * 8;
             if constexpr (kExt)
                 if (kcand && key == hi)
                     krow = kcand + qg * 8;
 #pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                if (key <= c_hi)
-                    ka[kb][s] = __builtin_nontemporal_load(
-                        reinterpret_cast<const bf16x8 *>(krow + s * 32));
-                else
-                    ka[kb][s] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            }
+            for (int s = 0; s < KS; ++s)
+                ka[kb][s] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(krow + s * 32));
         }
 #pragma unroll
         for (int it = 0; it < VIT; ++it) {
-            const int key = j0 + it * VPI + lane / LPK;
+            const int key = min(j0 + it * VPI + lane / LPK, c_hi);
             const int col = (lane % LPK) * 8;
             const uint16_t *vrow = vbase + cell(key) * D;
             if constexpr (kExt)
                 if (vcand && key == hi)
                     vrow = vcand;
-            if (key <= c_hi)
-                vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow + col));
-            else
-                vr[it] = u32x4{0u, 0u, 0u, 0u};
+            vr[it] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vrow + col));
         }
     };
 
@@ -235,13 +231,23 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     int r_cnt = 0, r_xor = 0, r_lo = INT_MAX, r_hi = -1;
 
-    bf16x8 ka[2][KS], kn[2][KS];
-    u32x4 vr[VIT], vn[VIT];
-    int j0 = c_lo + wave * kDecodeTile;
-    load_tile(j0, ka, vr);
-    for (; j0 <= c_hi; j0 += STEP) {
-        load_tile(j0 + STEP, kn, vn); // next tile, in flight during this one
+    // Wait until one tile's registers have landed.  The scheduling barrier
+    // keeps the next tile's loads behind the wait: each wavefront then has
+    // one tile (16 KiB at d = 128) in flight while it computes, ~32 MiB over
+    // the chip.  With two tiles per wavefront HBM delivered less.
+    auto wait_tile = [&](const bf16x8 (&ka)[2][KS], const u32x4 (&vr)[VIT]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < KS; ++s)
+                asm volatile("" ::"v"(ka[kb][s]));
+#pragma unroll
+        for (int it = 0; it < VIT; ++it)
+            asm volatile("" ::"v"(vr[it]));
+        __builtin_amdgcn_sched_barrier(0);
+    };
 
+    auto compute_tile = [&](int j0, const bf16x8 (&ka)[2][KS], const u32x4 (&vr)[VIT]) {
         // S^T = K . Q^T ; lane (hl, qg) gets keys kb*16 + qg*4 + i of head hl.
         f32x4 sacc[2];
 #pragma unroll
@@ -279,25 +285,35 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mn = fmaxf(m, tmax); // finite: key j0 is always permitted
-        const float alpha = fast_exp2(m - mn);
-        m = mn;
+        // Lazy rescale: the reference maximum m moves only when a head's new
+        // scores exceed it by more than 2^8, so every p = 2^(x - m) stays
+        // <= 256 and the accumulators are rescaled only on those tiles.  The
+        // partial's log2-sum-exp is m + log2(lsum) for whatever m is held,
+        // so the result is the same softmax.  Key j0 is always permitted, so
+        // a wavefront's first tile has a finite tmax and sets m.
+        const bool grow = tmax > m + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            const float mn = grow ? tmax : m;
+            const float alpha = grow ? fast_exp2(m - mn) : 1.f; // 0 when m was -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+                oacc[i] *= alpha;
+            m = mn;
+        }
         float psum = 0.f;
         uint32_t pw[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; i += 2) {
-                const float p0 = fast_exp2(x[kb][i] - mn);
-                const float p1 = fast_exp2(x[kb][i + 1] - mn);
+                const float p0 = fast_exp2(x[kb][i] - m);
+                const float p1 = fast_exp2(x[kb][i + 1] - m);
                 psum += p0 + p1;
                 pw[kb * 2 + i / 2] = pack_bf16x2(p0, p1);
             }
         const bf16x8 pb = __builtin_bit_cast(bf16x8, (uint4){pw[0], pw[1], pw[2], pw[3]});
-        lsum = fmaf(lsum, alpha, psum);
-#pragma unroll
-        for (int i = 0; i < DB; ++i)
-            oacc[i] *= alpha;
+        lsum += psum;
 
         if (kRecord) {
 #pragma unroll
@@ -331,15 +347,28 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
             oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, oacc[db], 0, 0, 0);
         }
+    };
 
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int s = 0; s < KS; ++s)
-                ka[kb][s] = kn[kb][s];
-#pragma unroll
-        for (int it = 0; it < VIT; ++it)
-            vr[it] = vn[it];
+    // Two register sets take alternate tiles, so no register copy (which
+    // would wait for the loads in flight) sits between tiles.
+    bf16x8 ka0[2][KS], ka1[2][KS];
+    u32x4 vr0[VIT], vr1[VIT];
+    int j0 = c_lo + wave * kDecodeTile;
+    if (j0 <= c_hi)
+        load_tile(j0, ka0, vr0);
+    while (j0 <= c_hi) {
+        wait_tile(ka0, vr0);
+        if (j0 + STEP <= c_hi)
+            load_tile(j0 + STEP, ka1, vr1);
+        compute_tile(j0, ka0, vr0);
+        j0 += STEP;
+        if (j0 > c_hi)
+            break;
+        wait_tile(ka1, vr1);
+        if (j0 + STEP <= c_hi)
+            load_tile(j0 + STEP, ka0, vr0);
+        compute_tile(j0, ka1, vr1);
+        j0 += STEP;
     }
 
     // Per-head running sum: add the 4 lane groups that share head hl.
@@ -449,6 +478,21 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
     const int64_t row = idx / Q4;
     const int c4 = static_cast<int>(idx % Q4) * 4;
     const int b = static_cast<int>(row / a.Hq);
+    const float *lse = a.lse_part + row * a.nsplit;
+    const float *op = a.o_part + row * a.nsplit * D + c4;
+    // The partial loads do not wait for the row length: all nsplit slots of
+    // the row are in the workspace, and only the first ns of them (those
+    // written by this call) are used.
+    constexpr int kPre = 8;
+    float lpre[kPre];
+    float4 opre[kPre];
+#pragma unroll
+    for (int s = 0; s < kPre; ++s) {
+        if (s < a.nsplit) {
+            lpre[s] = lse[s];
+            opre[s] = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
+        }
+    }
     const int nb = a.seqlens ? a.seqlens[b] : a.C;
     if (nb <= 0)
         return; // written by the split kernel
@@ -457,18 +501,12 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
     const int ns = (hi - lo) / a.chunk + 1;
     if (ns == 1)
         return; // finished by the split kernel
-    const float *lse = a.lse_part + row * a.nsplit;
-    const float *op = a.o_part + row * a.nsplit * D + c4;
-    // One pass with a running maximum: no load depends on another, so the
-    // partials of every chunk are in flight together.  Every chunk of a row
-    // with ns > 1 folded at least one key, so each lse_s is finite.
+    // One pass with a running maximum.  Every chunk of a row with ns > 1
+    // folded at least one key, so each lse_s is finite.
     float mx = -INFINITY;
     float den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) {
-        const float l = lse[s];
-        const float4 o = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
+    auto fold = [&](float l, float4 o) {
         const float mn = fmaxf(mx, l);
         const float sc = fast_exp2(mx - mn); // 0 on the first chunk (mx = -inf)
         const float w = fast_exp2(l - mn);
@@ -478,7 +516,13 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
         acc.z = fmaf(acc.z, sc, w * o.z);
         acc.w = fmaf(acc.w, sc, w * o.w);
         mx = mn;
-    }
+    };
+#pragma unroll
+    for (int s = 0; s < kPre; ++s)
+        if (s < ns)
+            fold(lpre[s], opre[s]);
+    for (int s = kPre; s < ns; ++s)
+        fold(lse[s], *reinterpret_cast<const float4 *>(op + (int64_t)s * D));
     const float inv = 1.f / den;
     uint2 pk;
     pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
@@ -506,21 +550,16 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window) {
     const int elig = (window > 0 && window < C) ? window : C;
     const int r = Hq / Hkv;
     p.nhc = (r + kDecodeHeads - 1) / kDecodeHeads;
-    // Aim for at least two 4-wavefront workgroups per compute unit on a
-    // 256-CU part, with as long a chunk as that allows (fewer partials).
+    // Aim for two 4-wavefront workgroups per compute unit on a 256-CU part
+    // (a streaming read peaks there), with chunks of at least one tile per
+    // wavefront.  The chunks split the range evenly: the kernel lasts as long
+    // as its longest chunk.
     const int64_t units = (int64_t)B * Hkv * p.nhc;
     const int64_t target = 512;
-    int tpw = 1;
-    for (int t = 16; t >= 1; t >>= 1) {
-        const int64_t chunk = (int64_t)kDecodeWaves * kDecodeTile * t;
-        const int64_t ns = (elig + chunk - 1) / chunk;
-        if (units * ns >= target) {
-            tpw = t;
-            break;
-        }
-    }
-    p.tiles_per_wave = tpw;
-    p.chunk = kDecodeWaves * kDecodeTile * tpw;
+    const int64_t step = (int64_t)kDecodeWaves * kDecodeTile;
+    int64_t ns = (target + units - 1) / units;
+    ns = std::max<int64_t>(1, std::min<int64_t>(ns, (elig + step - 1) / step));
+    p.chunk = static_cast<int>(std::max<int64_t>(step, (elig + ns - 1) / ns));
     p.nsplit = elig > 0 ? (elig + p.chunk - 1) / p.chunk : 0;
     const size_t rows = (size_t)B * Hq * (size_t)p.nsplit;
     p.o_off = 0;

@@ -40,13 +40,13 @@ struct Problem {
 
 // Split-K decode plan: the eligible key range of a row is cut into chunks of
 // `chunk` keys starting at the row's window start; each chunk is one
-// workgroup of 4 wavefronts, each wavefront taking 32-key tiles.
+// workgroup of 4 wavefronts, each wavefront taking 32-key tiles (the last tile
+// of a chunk may be partial: chunks are sized to split the range evenly).
 // Workspace layout: partial outputs [B, Hq, nsplit, d] fp32, their
 // log2-sum-exp values [B, Hq, nsplit] fp32 and index-set partials
 // [B, Hq, nsplit, 4] int32 (each region 256-byte aligned).
 struct DecodePlan {
-    int tiles_per_wave;
-    int chunk;    // keys per workgroup = 4 * 32 * tiles_per_wave
+    int chunk;    // keys per workgroup, at least 128
     int nsplit;   // chunks per row at the longest eligible range
     int nhc;      // head chunks of up to 16 query heads per KV group
     size_t o_off, lse_off, rec_off, bytes;
