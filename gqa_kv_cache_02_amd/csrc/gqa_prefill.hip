@@ -102,10 +102,183 @@ template <int D> struct PrefillLayout {
     __device__ static int fv(int r) { return ((r / RPL) % (4 / RPL)) * 4; }
 };
 
+// Per-wavefront tile math: one wavefront owns 32 query rows (lane l holds row
+// l & 31 together with lane l ^ 32) and works through one 64-key tile in
+// three steps -- scores, softmax, P.V.
+template <int D, bool kRecord> struct TileMath {
+    using L = PrefillLayout<D>;
+    static constexpr int KS = D / 16; // 16-feature k-steps of Q.K (32x32x16)
+    static constexpr int DB = D / 32; // 32-column blocks of P.V
+    static constexpr int CPR = L::CPR;
+
+    __device__ __forceinline__ static bf16x8 kread(const unsigned char *kst, int s, int kb, int lane) {
+        const int row = kb * 32 + (lane & 31);
+        const int c = 2 * s + (lane >> 5);
+        return *reinterpret_cast<const bf16x8 *>(kst + (row * CPR + (c ^ L::fk(row))) * 16);
+    }
+
+    // S^T = K . Q^T for the tile's two 32-key blocks, chains interleaved.
+    // The K operands are read one k-step ahead of their MFMAs; the
+    // scheduling barriers keep the compiler from hoisting every read of the
+    // tile up front, which would hold 16 operands in registers.
+    __device__ __forceinline__ static void scores(const unsigned char *kst, const bf16x8 (&qb)[KS],
+                                                  f32x16 (&sacc)[2], int lane) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                sacc[kb][e] = 0.f;
+        bf16x8 kc0 = kread(kst, 0, 0, lane), kc1 = kread(kst, 0, 1, lane);
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            bf16x8 kn0 = kc0, kn1 = kc1;
+            if (s + 1 < KS) {
+                kn0 = kread(kst, s + 1, 0, lane);
+                kn1 = kread(kst, s + 1, 1, lane);
+            }
+            sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc0, qb[s], sacc[0], 0, 0, 0);
+            sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc1, qb[s], sacc[1], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            kc0 = kn0;
+            kc1 = kn1;
+        }
+    }
+
+    // Mask (edge tiles only), the row's max, lazy rescale, exponentials and
+    // the bf16 P^T operands (plus the index-set records).
+    template <bool full>
+    __device__ __forceinline__ static void softmax(f32x16 (&sacc)[2], bf16x8 (&pb)[2][2],
+                                                   f32x16 (&oacc)[DB], float &m, float &lsum,
+                                                   int &r_cnt, int &r_xor, int &r_lo, int &r_hi,
+                                                   int j0, int my_pos, int lo_row, int lane,
+                                                   float scale_log2) {
+        const int qq = lane >> 5;
+        // Mask (diagonal, window-edge and padded-row tiles only) and the
+        // row's max.  Lane l holds row r0 + (l & 31) and keys
+        // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.  Scores stay unscaled;
+        // the scale (>= 0 after the sign flip of Q) is folded into one FMA
+        // in front of the exponential.
+        float tmax = -INFINITY;
+        if constexpr (full) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    tmax = fmaxf(tmax, sacc[kb][v]);
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
+                    // lo_row is INT_MAX on inactive rows: nothing kept
+                    const bool keep = (j <= my_pos) && (j >= lo_row);
+                    sacc[kb][v] = keep ? sacc[kb][v] : -INFINITY;
+                    tmax = fmaxf(tmax, sacc[kb][v]);
+                }
+        }
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
+                                                             __float_as_uint(tmax), false, false);
+            tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])); // lanes l and l^32
+        }
+        tmax = (tmax == -INFINITY) ? -INFINITY : tmax * scale_log2;
+
+        // Lazy rescale: the reference maximum m only moves when a row's new
+        // scores exceed it by more than 2^8, so every p = 2^(x - m) stays
+        // <= 256 and the accumulators are touched only on those rare
+        // tiles.  The final division by the running sum uses the same m,
+        // so the result is the same softmax.
+        const bool grow = tmax > m + 8.f;
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+            // rows that do not grow keep m and alpha = 1 (m may still be
+            // -inf there, where m - m would be NaN)
+            const float mn = grow ? tmax : m;
+            const float alpha = grow ? fast_exp2(m - mn) : 1.f; // 0 when m was -inf
+            lsum *= alpha;
+#pragma unroll
+            for (int i = 0; i < DB; ++i)
+#pragma unroll
+                for (int e = 0; e < 16; ++e)
+                    oacc[i][e] *= alpha;
+            m = mn;
+        }
+        const float mneg = (m == -INFINITY) ? 0.f : -m;
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int stp = 0; stp < 2; ++stp) {
+                uint32_t w[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    const int v = 8 * stp + 2 * e2;
+                    float p0 = fast_exp2(fmaf(sacc[kb][v], scale_log2, mneg));
+                    float p1 = fast_exp2(fmaf(sacc[kb][v + 1], scale_log2, mneg));
+                    if constexpr (!full) { // masked cells contribute exactly 0
+                        p0 = (sacc[kb][v] == -INFINITY) ? 0.f : p0;
+                        p1 = (sacc[kb][v + 1] == -INFINITY) ? 0.f : p1;
+                    }
+                    psum += p0 + p1;
+                    w[e2] = pack_bf16x2(p0, p1);
+                    if (kRecord) {
+#pragma unroll
+                        for (int u = 0; u < 2; ++u) {
+                            if (sacc[kb][v + u] != -INFINITY) { // a permitted cell
+                                const int j = j0 + kb * 32 + 8 * ((v + u) / 4) + 4 * qq + ((v + u) % 4);
+                                r_cnt += 1;
+                                r_xor ^= j;
+                                r_lo = min(r_lo, j);
+                                r_hi = max(r_hi, j);
+                            }
+                        }
+                    }
+                }
+                pb[kb][stp] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
+            }
+        lsum += psum;
+    }
+
+    // O^T += V^T . P^T for the tile.
+    __device__ __forceinline__ static void pv(const unsigned char *vst, const bf16x8 (&pb)[2][2],
+                                              f32x16 (&oacc)[DB], int lane) {
+        const int qq = lane >> 5;
+        const int gl = lane & 15;
+        const int cgrp = (lane >> 4) & 1; // which 16 columns of a 32-column block
+        // O^T += V^T . P^T.  For key block kb and k-step stp, P^T k-slot
+        // 8*(l>>5) + e is key kb*32 + 16*stp + 8*(e/4) + 4*(l>>5) + e%4, so
+        // V^T needs two runs of 4 consecutive keys per lane: one
+        // transposing LDS read per run.  In each 16-lane group, lane j
+        // supplies row k0 + j/4, columns c0 + 4*(j%4) .. +3 and receives
+        // column c0 + (lane & 15).
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int stp = 0; stp < 2; ++stp) {
+                const int k0 = kb * 32 + 16 * stp + 4 * qq;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) {
+                    const int col = db * 32 + 16 * cgrp + 4 * (gl & 3);
+                    const int ra = k0 + (gl >> 2);
+                    const int rb2 = ra + 8;
+                    const unsigned char *pa =
+                        vst + (ra * CPR + ((col >> 3) ^ L::fv(ra))) * 16 + (col & 7) * 2;
+                    const unsigned char *pb2 =
+                        vst + (rb2 * CPR + ((col >> 3) ^ L::fv(rb2))) * 16 + (col & 7) * 2;
+                    const s16x4 lo4 = ds_read_tr(reinterpret_cast<const uint16_t *>(pa));
+                    const s16x4 hi4 = ds_read_tr(reinterpret_cast<const uint16_t *>(pb2));
+                    const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+                    oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][stp], oacc[db], 0, 0, 0);
+                }
+            }
+    }
+};
+
 template <int D, bool kRecord>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a) {
     using L = PrefillLayout<D>;
+    using TM = TileMath<D, kRecord>;
     constexpr int KS = D / 16;   // 16-feature k-steps of Q.K (32x32x16)
     constexpr int DB = D / 32;   // 32-column blocks of P.V
     constexpr int CPR = L::CPR;
@@ -326,8 +499,6 @@ void prefill_mfma_kernel(PrefillArgs a) {
     float lsum = 0.f;    // this lane's share of the running sum
     int r_cnt = 0, r_xor = 0, r_lo = INT_MAX, r_hi = -1;
     const int qq = lane >> 5;
-    const int gl = lane & 15;
-    const int cgrp = (lane >> 4) & 1; // which 16 columns of a 32-column block
 
     // One tile: start the direct loads of the next tile into the other stage,
     // compute on this stage, then wait until every wavefront's loads landed
@@ -344,149 +515,13 @@ void prefill_mfma_kernel(PrefillArgs a) {
         // instantiations so that interior tiles carry no masking code.
         auto compute = [&](auto full_tag) {
             constexpr bool full = decltype(full_tag)::value;
-            // S^T = K . Q^T for two 32-key blocks, chains interleaved.
             f32x16 sacc[2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    sacc[kb][e] = 0.f;
-            auto kread = [&](int s, int kb) {
-                const int row = kb * 32 + (lane & 31);
-                const int c = 2 * s + qq;
-                return *reinterpret_cast<const bf16x8 *>(kst + (row * CPR + (c ^ L::fk(row))) * 16);
-            };
-            // K operands are read one k-step ahead of their MFMAs; the
-            // scheduling barriers keep the compiler from hoisting every read
-            // of the tile up front, which would hold 16 operands in registers.
-            bf16x8 kc0 = kread(0, 0), kc1 = kread(0, 1);
-#pragma unroll
-            for (int s = 0; s < KS; ++s) {
-                bf16x8 kn0 = kc0, kn1 = kc1;
-                if (s + 1 < KS) {
-                    kn0 = kread(s + 1, 0);
-                    kn1 = kread(s + 1, 1);
-                }
-                sacc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc0, qb[s], sacc[0], 0, 0, 0);
-                sacc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kc1, qb[s], sacc[1], 0, 0, 0);
-                __builtin_amdgcn_sched_barrier(0);
-                kc0 = kn0;
-                kc1 = kn1;
-            }
-
-            // Mask (diagonal, window-edge and padded-row tiles only) and the
-            // row's max.  Lane l holds row r0 + (l & 31) and keys
-            // j0 + kb*32 + 8*(v/4) + 4*(l>>5) + v%4.  Scores stay unscaled;
-            // the scale (>= 0 after the sign flip of Q) is folded into one FMA
-            // in front of the exponential.
-            float tmax = -INFINITY;
-            if constexpr (full) {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        tmax = fmaxf(tmax, sacc[kb][v]);
-            } else {
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int j = j0 + kb * 32 + 8 * (v / 4) + 4 * qq + (v % 4);
-                        // lo_row is INT_MAX on inactive rows: nothing kept
-                        const bool keep = (j <= my_pos) && (j >= lo_row);
-                        sacc[kb][v] = keep ? sacc[kb][v] : -INFINITY;
-                        tmax = fmaxf(tmax, sacc[kb][v]);
-                    }
-            }
-            {
-                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(tmax),
-                                                                 __float_as_uint(tmax), false, false);
-                tmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])); // lanes l and l^32
-            }
-            tmax = (tmax == -INFINITY) ? -INFINITY : tmax * a.scale_log2;
-
-            // Lazy rescale: the reference maximum m only moves when a row's new
-            // scores exceed it by more than 2^8, so every p = 2^(x - m) stays
-            // <= 256 and the accumulators are touched only on those rare
-            // tiles.  The final division by the running sum uses the same m,
-            // so the result is the same softmax.
-            const bool grow = tmax > m + 8.f;
-            if (__builtin_amdgcn_ballot_w64(grow)) {
-                // rows that do not grow keep m and alpha = 1 (m may still be
-                // -inf there, where m - m would be NaN)
-                const float mn = grow ? tmax : m;
-                const float alpha = grow ? fast_exp2(m - mn) : 1.f; // 0 when m was -inf
-                lsum *= alpha;
-#pragma unroll
-                for (int i = 0; i < DB; ++i)
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        oacc[i][e] *= alpha;
-                m = mn;
-            }
-            const float mneg = (m == -INFINITY) ? 0.f : -m;
-            float psum = 0.f;
             bf16x8 pb[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int stp = 0; stp < 2; ++stp) {
-                    uint32_t w[4];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        const int v = 8 * stp + 2 * e2;
-                        float p0 = fast_exp2(fmaf(sacc[kb][v], a.scale_log2, mneg));
-                        float p1 = fast_exp2(fmaf(sacc[kb][v + 1], a.scale_log2, mneg));
-                        if constexpr (!full) { // masked cells contribute exactly 0
-                            p0 = (sacc[kb][v] == -INFINITY) ? 0.f : p0;
-                            p1 = (sacc[kb][v + 1] == -INFINITY) ? 0.f : p1;
-                        }
-                        psum += p0 + p1;
-                        w[e2] = pack_bf16x2(p0, p1);
-                        if (kRecord) {
-#pragma unroll
-                            for (int u = 0; u < 2; ++u) {
-                                if (sacc[kb][v + u] != -INFINITY) { // a permitted cell
-                                    const int j = j0 + kb * 32 + 8 * ((v + u) / 4) + 4 * qq + ((v + u) % 4);
-                                    r_cnt += 1;
-                                    r_xor ^= j;
-                                    r_lo = min(r_lo, j);
-                                    r_hi = max(r_hi, j);
-                                }
-                            }
-                        }
-                    }
-                    pb[kb][stp] = __builtin_bit_cast(bf16x8, (uint4){w[0], w[1], w[2], w[3]});
-                }
-            lsum += psum;
-
-            // O^T += V^T . P^T.  For key block kb and k-step stp, P^T k-slot
-            // 8*(l>>5) + e is key kb*32 + 16*stp + 8*(e/4) + 4*(l>>5) + e%4, so
-            // V^T needs two runs of 4 consecutive keys per lane: one
-            // transposing LDS read per run.  In each 16-lane group, lane j
-            // supplies row k0 + j/4, columns c0 + 4*(j%4) .. +3 and receives
-            // column c0 + (lane & 15).
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int stp = 0; stp < 2; ++stp) {
-                    const int k0 = kb * 32 + 16 * stp + 4 * qq;
-#pragma unroll
-                    for (int db = 0; db < DB; ++db) {
-                        const int col = db * 32 + 16 * cgrp + 4 * (gl & 3);
-                        const int ra = k0 + (gl >> 2);
-                        const int rb2 = ra + 8;
-                        const unsigned char *pa =
-                            vst + (ra * CPR + ((col >> 3) ^ L::fv(ra))) * 16 + (col & 7) * 2;
-                        const unsigned char *pb2 =
-                            vst + (rb2 * CPR + ((col >> 3) ^ L::fv(rb2))) * 16 + (col & 7) * 2;
-                        const s16x4 lo4 = ds_read_tr(reinterpret_cast<const uint16_t *>(pa));
-                        const s16x4 hi4 = ds_read_tr(reinterpret_cast<const uint16_t *>(pb2));
-                        const bf16x8 va = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                        oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[kb][stp], oacc[db], 0, 0, 0);
-                    }
-                }
-                };
+            TM::scores(kst, qb, sacc, lane);
+            TM::template softmax<full>(sacc, pb, oacc, m, lsum, r_cnt, r_xor, r_lo, r_hi, j0, my_pos,
+                                       lo_row, lane, a.scale_log2);
+            TM::pv(vst, pb, oacc, lane);
+        };
         if (work) {
             if (w_all && (j0 + kPBN - 1 <= w_first) && (j0 >= w_lo_last))
                 compute(std::true_type{});
