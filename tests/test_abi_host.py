@@ -206,3 +206,31 @@ def test_refusals_decode_cache():
     L = gqa.lib()
     need = L.gqa_decode_workspace_bytes(2, 64, 8, 2, 128, 16, 1)
     assert _dcache(wsb=need - 1) == WORKSPACE
+
+
+def _decode_plan_bytes(B, C, hq, hkv, d, window):
+    """The split plan the decode kernel follows, restated: about 512
+    workgroups (two per CU on 256 CUs), at most one split per 128 keys (a
+    32-key tile per wavefront), the permitted range cut evenly."""
+    elig = window if 0 < window < C else C
+    units = B * hkv * -(-(hq // hkv) // 16)
+    ns = max(1, min(-(-512 // units), -(-elig // 128)))
+    chunk = max(128, -(-elig // ns))
+    nsplit = -(-elig // chunk) if elig > 0 else 0
+    rows = B * hq * nsplit
+    a256 = lambda x: (x + 255) // 256 * 256
+    return a256(rows * d * 4) + a256(rows * 4) + a256(rows * 16), nsplit, chunk
+
+
+def test_decode_plan_even_chunks():
+    L = gqa.lib()
+    shapes = [(8, 8000, 32, 8, 128, -1), (1, 200, 8, 8, 64, -1), (64, 8000, 32, 8, 128, -1),
+              (2, 5000, 64, 2, 64, -1), (4, 10000, 8, 2, 128, 1000), (32, 32768, 8, 2, 64, 4096),
+              (3, 129, 6, 2, 128, -1), (1, 1, 4, 2, 64, -1), (5, 777, 12, 3, 64, 300)]
+    for B, C, hq, hkv, d, w in shapes:
+        want, nsplit, chunk = _decode_plan_bytes(B, C, hq, hkv, d, w)
+        assert L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, 1) == want, (B, C, hq, hkv, d, w)
+        elig = w if 0 < w < C else C
+        assert chunk >= 128 and (nsplit - 1) * chunk < elig <= nsplit * chunk
+    # the headline decode: 8 chunks of 1000 keys, not 7 of 1024 and one of 832
+    assert _decode_plan_bytes(8, 8000, 32, 8, 128, -1)[1:] == (8, 1000)
