@@ -15,11 +15,13 @@ Prints ONE JSON line.
   value          algorithmic HBM GB/s (K/V cells read once per KV group, plus
                  Q read and O written) over K back-to-back timed steps.
   roofline       the decode call's own duration (HIP events recorded on the
-                 launch stream around each call, second pass), against the
-                 8 TB/s HBM3E peak.  `traffic` is the HBM bytes per call that
-                 rocprofv3 counters measured (profiles/, scaled by a plain
-                 copy of known size), reported only while the kernel source
-                 still has the hash the counters were taken with.
+                 launch stream around each call, second pass; mean, minimum
+                 and p10/p50/p90), against the 8 TB/s HBM3E peak.  `traffic`
+                 is the HBM bytes per call that rocprofv3 counters measured
+                 (profiles/, scaled by a plain copy of known size), reported
+                 only while the kernel source still has the hash the counters
+                 were taken with.  `hbm_copy_reference_gbs` is a live 1 GiB
+                 device copy; frac_of_measured_copy is `value` against it.
   prefill        causal prefill B=1, T=4096, Hq=32, Hkv=8, d=128: TFLOP/s of
                  the permitted pairs (4*d flops each) against 2.5 PFLOP/s
                  dense bf16 MFMA.
@@ -31,7 +33,8 @@ Prints ONE JSON line.
                  lengths in [1, 32768]): GB/s of the K/V cells in each row's
                  window read once per KV group, against 8 TB/s.
   cpu_baseline   the fp64 oracle (plain C, OpenMP) on the host cores, on the
-                 same decode workload.
+                 same decode workload; with the CPU model, the process's
+                 affinity set and a one-thread figure on one batch row.
 """
 from __future__ import annotations
 
@@ -128,8 +131,11 @@ def bench_decode(torch, gqa, synth, steps, warmup):
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     per_call = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+    srt = sorted(per_call)
+    pct = lambda f: srt[min(steps - 1, int(f * steps))]
     return dict(cfg=cfg, kernel=kernel, ms=ms, wall_s=wall,
                 avg_call_ms=sum(per_call) / steps, min_call_ms=min(per_call),
+                p10_call_ms=pct(0.10), p50_call_ms=pct(0.50), p90_call_ms=pct(0.90),
                 nbytes=decode_bytes(B, hq, hkv, d, n), q=q, k=k0, v=v0, seqlens=[n] * B)
 
 
@@ -266,8 +272,21 @@ def hbm_copy_reference(torch, nbytes=1 << 30, reps=10):
     return round(2 * nbytes / (ms * 1e-3) / 1e9, 1)
 
 
-def cpu_baseline(r, budget_s=12.0):
-    """The fp64 oracle as it stands, on the host cores, on the decode workload."""
+def _cpu_model():
+    try:
+        for ln in open("/proc/cpuinfo"):
+            if ln.startswith("model name"):
+                return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(r, budget_s=11.0):
+    """The fp64 oracle as it stands, on the host cores, on the decode workload;
+    plus one thread on batch row 0 (1/8 of the bytes), scaled to the whole."""
+    import ctypes
+
     import numpy as np
 
     import oracle
@@ -275,19 +294,41 @@ def cpu_baseline(r, budget_s=12.0):
     q = r["q"].float().cpu().numpy().astype(np.float64)
     k = r["k"].float().cpu().numpy().astype(np.float64)
     v = r["v"].float().cpu().numpy().astype(np.float64)
-    oracle.lib()
+    L = oracle.lib()
     runs, t_total = 0, 0.0
-    while t_total < budget_s and runs < 400:
+    while t_total < budget_s and runs < 1000:
         t0 = time.perf_counter()
         oracle.decode(q, k, v, seqlens=r["seqlens"])
         t_total += time.perf_counter() - t0
         runs += 1
     per = t_total / runs
-    return dict(value=round(r["nbytes"] / per / 1e9, 3), unit="GB/s", cores=oracle.threads(),
+    cores = oracle.threads()
+    # one thread, one batch row
+    set_threads = L.omp_set_num_threads
+    set_threads.argtypes = [ctypes.c_int]
+    set_threads(1)
+    try:
+        q1, k1, v1 = q[:1].copy(), k[:1].copy(), v[:1].copy()
+        runs1, t1 = 0, 0.0
+        while t1 < 1.5 and runs1 < 100:
+            t0 = time.perf_counter()
+            oracle.decode(q1, k1, v1, seqlens=r["seqlens"][:1])
+            t1 += time.perf_counter() - t0
+            runs1 += 1
+    finally:
+        set_threads(cores)
+    per1 = t1 / runs1
+    B = q.shape[0]
+    return dict(value=round(r["nbytes"] / per / 1e9, 3), unit="GB/s", cores=cores,
                 kind="oracle",
                 sample=f"the whole decode workload (B=8, Hq=32, Hkv=8, d=128, 8000 cells) in "
                        f"fp64, {runs} runs of {per:.4f} s; inputs converted to float64 "
-                       "before timing")
+                       "before timing",
+                affinity_cores=len(os.sched_getaffinity(0)), cpu_model=_cpu_model(),
+                single_thread={"value": round(r["nbytes"] / B / per1 / 1e9, 4), "unit": "GB/s",
+                               "sample": f"batch row 0 of {B} (1/{B} of the bytes), one thread, "
+                                         f"{runs1} runs of {per1:.4f} s; the rate holds for the "
+                                         "whole workload, whose rows are independent"})
 
 
 def main():
@@ -340,10 +381,14 @@ def main():
                      "bytes_per_launch": r["nbytes"],
                      "avg_launch_ms": round(r["avg_call_ms"], 5),
                      "min_launch_ms": round(r["min_call_ms"], 5),
+                     "p10_p50_p90_launch_ms": [round(r["p10_call_ms"], 5), round(r["p50_call_ms"], 5),
+                                               round(r["p90_call_ms"], 5)],
                      "kernel": "decode call = decode_kernel (split) + decode_merge_kernel",
                      "timing": "HIP events on the launch stream around each decode call"},
     }
-    line["roofline"]["hbm_copy_reference_gbs"] = hbm_copy_reference(torch)
+    copy_gbs = hbm_copy_reference(torch)
+    line["roofline"]["hbm_copy_reference_gbs"] = copy_gbs
+    line["frac_of_measured_copy"] = round(gbs / copy_gbs, 4)
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3)
         line["prefix_prefill"] = bench_prefix(torch, gqa, synth, max(10, args.steps // 10), 3)
