@@ -32,6 +32,12 @@ Prints ONE JSON line.
                  cell committed in the call (B=32, Hq=8, Hkv=2, d=64, ragged
                  lengths in [1, 32768]): GB/s of the K/V cells in each row's
                  window read once per KV group, against 8 TB/s.
+  decode_sweep   the endpoint sweep B=16, Hq=8, d=128, 8000 cells at Hkv = 8,
+                 2, 1 (MHA, GQA, MQA): GB/s of K/V read once per KV group.
+  ragged_window_decode  B=32, Hq=8, Hkv=2, d=64, lengths in [1, 32768],
+                 window 4096, linear cache: GB/s of the cells in the windows.
+  small_f32_prefill  the fp32 prefill B=1, T=16, Hq=4, Hkv=2, d=8: us per
+                 call (latency only), without a window and with window 2.
   cpu_baseline   the fp64 oracle (plain C, OpenMP) on the host cores, on the
                  same decode workload; with the CPU model, the process's
                  affinity set and a one-thread figure on one batch row.
@@ -241,6 +247,88 @@ def bench_ring(torch, gqa, synth, steps, warmup):
                 timing="HIP events on the launch stream around each call")
 
 
+def bench_sweep(torch, gqa, synth, steps, warmup):
+    """Endpoint sweep: B=16, Hq=8, d=128, 8000 cached cells; MHA, GQA group 4
+    and MQA.  A K/V copy holds 524, 131 or 66 MB; 4 copies rotate for Hkv >= 2
+    and 6 for Hkv = 1, so no step finds its cache in the 256 MB Infinity Cache
+    left by the previous ones."""
+    cfg = synth.CONFIGS["decode_sweep_b16_hq8_d128_n8000"]
+    B, hq, d, n = cfg["B"], cfg["Hq"], cfg["d"], cfg["n"]
+    dev = torch.device("cuda:0")
+    res = []
+    for hkv in cfg["Hkv"]:
+        copies = 4 if hkv >= 2 else 6
+        q, k0, v0 = synth.decode_inputs(B, n, hq, hkv, d, torch.bfloat16, cfg["seed"], dev)
+        ks, vs = [k0], [v0]
+        for i in range(1, copies):
+            _, k, v = synth.decode_inputs(B, n, hq, hkv, d, torch.bfloat16, cfg["seed"] + 100 * i, dev)
+            ks.append(k)
+            vs.append(v)
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, n, hq, hkv, d)), dtype=torch.uint8,
+                         device=dev)
+        ms = _time_calls(torch, lambda i: gqa.decode(q, ks[i % copies], vs[i % copies], out=out,
+                                                     workspace=ws), steps, warmup)
+        nbytes = decode_bytes(B, hq, hkv, d, n)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res.append(dict(Hkv=hkv, ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
+                        frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                        tokens_per_s=round(B / (ms * 1e-3), 1)))
+        del ks, vs, q, k0, v0
+    return dict(workload="gqa_decode_sweep_b16_hq8_d128_n8000_bf16", results=res,
+                timing="HIP events on the launch stream around each call")
+
+
+def bench_ragged_window(torch, gqa, synth, steps, warmup):
+    """Ragged sliding-window decode over a linear cache: B=32, Hq=8, Hkv=2,
+    d=64, lengths uniform in [1, 32768], window 4096.  GB/s of the K/V cells
+    inside each row's window, read once per KV group; 6 rotated copies."""
+    cfg = synth.CONFIGS["decode_ragged_b32_hq8_hkv2_d64_w4096"]
+    B, hq, hkv, d, C, w = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["C"], cfg["window"]
+    lo, hi = cfg["n"]
+    dev = torch.device("cuda:0")
+    lens = synth.ragged_lengths(B, lo, hi, cfg["seed"])
+    seqlens = lens.to(dev)
+    copies = 6
+    q, k0, v0 = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, cfg["seed"], dev)
+    ks, vs = [k0], [v0]
+    for i in range(1, copies):
+        _, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, cfg["seed"] + 100 * i, dev)
+        ks.append(k)
+        vs.append(v)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, C, hq, hkv, d, w)), dtype=torch.uint8,
+                     device=dev)
+    ms = _time_calls(torch, lambda i: gqa.decode(q, ks[i % copies], vs[i % copies],
+                                                 seqlens=seqlens, window=w, out=out,
+                                                 workspace=ws), steps, warmup)
+    cells = int(sum(min(int(n), w) for n in lens.tolist()))
+    nbytes = 2 * hkv * cells * d * 2 + 2 * B * hq * d * 2
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return dict(workload="gqa_decode_ragged_b32_hq8_hkv2_d64_w4096_bf16",
+                ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
+                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
+                timing="HIP events on the launch stream around each call")
+
+
+def bench_small_f32(torch, gqa, synth, steps, warmup):
+    """The small fp32 causal prefill (B=1, T=16, Hq=4, Hkv=2, d=8): latency
+    only, with no window and with window 2."""
+    cfg = synth.CONFIGS["prefill_f32_small"]
+    B, T, hq, hkv, d = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    dev = torch.device("cuda:0")
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.float32, cfg["seed"], dev)
+    out = torch.empty((B, T, hq, d), dtype=torch.float32, device=dev)
+    res = {}
+    for w in cfg["windows"]:
+        ms = _time_calls(torch, lambda i: gqa.prefill(q, k, v, window=w, out=out), steps, warmup)
+        res["no_window" if w is None else f"window_{w}"] = round(ms * 1e3, 2)
+    return dict(workload="gqa_prefill_b1_t16_hq4_hkv2_d8_causal_f32",
+                kernel=gqa.prefill_kernel(B, T, T, hq, hkv, d, dtype=torch.float32),
+                us_per_call=res, timing="HIP events on the launch stream around each call")
+
+
 def copy_calibration(torch):
     """A plain device copy of COPY_CAL_BYTES, so that rocprofv3's FETCH_SIZE
     and WRITE_SIZE counters can be scaled against a known transfer."""
@@ -393,6 +481,9 @@ def main():
         line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3)
         line["prefix_prefill"] = bench_prefix(torch, gqa, synth, max(10, args.steps // 10), 3)
     line["ring_decode"] = bench_ring(torch, gqa, synth, max(20, args.steps // 2), 10)
+    line["decode_sweep"] = bench_sweep(torch, gqa, synth, max(20, args.steps // 2), 10)
+    line["ragged_window_decode"] = bench_ragged_window(torch, gqa, synth, max(20, args.steps // 2), 10)
+    line["small_f32_prefill"] = bench_small_f32(torch, gqa, synth, max(20, args.steps // 2), 10)
     if args.copy_calibration:
         copy_calibration(torch)
         line["copy_calibration_bytes"] = COPY_CAL_BYTES
