@@ -480,17 +480,18 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
     const int b = static_cast<int>(row / a.Hq);
     const float *lse = a.lse_part + row * a.nsplit;
     const float *op = a.o_part + row * a.nsplit * D + c4;
-    // The partial loads do not wait for the row length: all nsplit slots of
-    // the row are in the workspace, and only the first ns of them (those
-    // written by this call) are used.
-    constexpr int kPre = 8;
-    float lpre[kPre];
-    float4 opre[kPre];
+    // Partials are loaded in unrolled chunks of kChunk splits, every load of
+    // a chunk in flight together.  The first chunk does not wait for the row
+    // length: all nsplit slots of the row are in the workspace, and only the
+    // first ns of them (those written by this call) are used.
+    constexpr int kChunk = 8;
+    float lc[kChunk];
+    float4 oc[kChunk];
 #pragma unroll
-    for (int s = 0; s < kPre; ++s) {
-        if (s < a.nsplit) {
-            lpre[s] = lse[s];
-            opre[s] = *reinterpret_cast<const float4 *>(op + (int64_t)s * D);
+    for (int i = 0; i < kChunk; ++i) {
+        if (i < a.nsplit) {
+            lc[i] = lse[i];
+            oc[i] = *reinterpret_cast<const float4 *>(op + (int64_t)i * D);
         }
     }
     const int nb = a.seqlens ? a.seqlens[b] : a.C;
@@ -506,23 +507,33 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
     float mx = -INFINITY;
     float den = 0.f;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto fold = [&](float l, float4 o) {
-        const float mn = fmaxf(mx, l);
-        const float sc = fast_exp2(mx - mn); // 0 on the first chunk (mx = -inf)
-        const float w = fast_exp2(l - mn);
-        den = fmaf(den, sc, w);
-        acc.x = fmaf(acc.x, sc, w * o.x);
-        acc.y = fmaf(acc.y, sc, w * o.y);
-        acc.z = fmaf(acc.z, sc, w * o.z);
-        acc.w = fmaf(acc.w, sc, w * o.w);
-        mx = mn;
-    };
+    for (int s0 = 0; s0 < ns; s0 += kChunk) {
+        if (s0 > 0) {
 #pragma unroll
-    for (int s = 0; s < kPre; ++s)
-        if (s < ns)
-            fold(lpre[s], opre[s]);
-    for (int s = kPre; s < ns; ++s)
-        fold(lse[s], *reinterpret_cast<const float4 *>(op + (int64_t)s * D));
+            for (int i = 0; i < kChunk; ++i) {
+                if (s0 + i < ns) {
+                    lc[i] = lse[s0 + i];
+                    oc[i] = *reinterpret_cast<const float4 *>(op + (int64_t)(s0 + i) * D);
+                }
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i) {
+            if (s0 + i < ns) {
+                const float l = lc[i];
+                const float4 o = oc[i];
+                const float mn = fmaxf(mx, l);
+                const float sc = fast_exp2(mx - mn); // 0 on the first chunk (mx = -inf)
+                const float w = fast_exp2(l - mn);
+                den = fmaf(den, sc, w);
+                acc.x = fmaf(acc.x, sc, w * o.x);
+                acc.y = fmaf(acc.y, sc, w * o.y);
+                acc.z = fmaf(acc.z, sc, w * o.z);
+                acc.w = fmaf(acc.w, sc, w * o.w);
+                mx = mn;
+            }
+        }
+    }
     const float inv = 1.f / den;
     uint2 pk;
     pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
