@@ -561,15 +561,27 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window) {
     const int elig = (window > 0 && window < C) ? window : C;
     const int r = Hq / Hkv;
     p.nhc = (r + kDecodeHeads - 1) / kDecodeHeads;
-    // Aim for two 4-wavefront workgroups per compute unit on a 256-CU part
-    // (a streaming read peaks there), with chunks of at least one tile per
-    // wavefront.  The chunks split the range evenly: the kernel lasts as long
-    // as its longest chunk.
+    // Number of splits ns.  The launch runs ceil(units * ns / 256) rounds of
+    // one 4-wavefront workgroup per CU (256 CUs), each round 1/ns of a row's
+    // range, so its time goes as rounds(ns) / ns: pick the ns that minimises
+    // it, ties to fewer splits (less to merge).  At most two workgroups per
+    // CU in all: with one tile in flight per wavefront, one workgroup per CU
+    // holds ~16 MiB of reads in flight over the chip, where a streaming read
+    // peaks, and more is slower.  Chunks hold at least one tile per wavefront
+    // and split the range evenly: a round lasts as long as its longest chunk.
     const int64_t units = (int64_t)B * Hkv * p.nhc;
-    const int64_t target = 512;
+    const int64_t cus = kDecodeCUs;
     const int64_t step = (int64_t)kDecodeWaves * kDecodeTile;
-    int64_t ns = (target + units - 1) / units;
-    ns = std::max<int64_t>(1, std::min<int64_t>(ns, (elig + step - 1) / step));
+    const int64_t max_ns = std::max<int64_t>(
+        1, std::min<int64_t>((elig + step - 1) / step, units > 0 ? 2 * cus / units : 1));
+    int64_t ns = 1, ns_rounds = units > 0 ? (units + cus - 1) / cus : 1;
+    for (int64_t c = 2; c <= max_ns; ++c) {
+        const int64_t rounds = (units * c + cus - 1) / cus;
+        if (rounds * ns < ns_rounds * c) { // rounds / c < ns_rounds / ns
+            ns = c;
+            ns_rounds = rounds;
+        }
+    }
     p.chunk = static_cast<int>(std::max<int64_t>(step, (elig + ns - 1) / ns));
     p.nsplit = elig > 0 ? (elig + p.chunk - 1) / p.chunk : 0;
     const size_t rows = (size_t)B * Hq * (size_t)p.nsplit;

@@ -55,6 +55,7 @@ struct DecodePlan {
 constexpr int kDecodeTile = 32;
 constexpr int kDecodeWaves = 4;
 constexpr int kDecodeHeads = 16;
+constexpr int kDecodeCUs = 256; // compute units of the MI355X the decode plan targets
 
 DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window);
 

@@ -209,12 +209,16 @@ def test_refusals_decode_cache():
 
 
 def _decode_plan_bytes(B, C, hq, hkv, d, window):
-    """The split plan the decode kernel follows, restated: about 512
-    workgroups (two per CU on 256 CUs), at most one split per 128 keys (a
-    32-key tile per wavefront), the permitted range cut evenly."""
+    """The split plan the decode kernel follows, restated: the number of
+    splits ns minimises rounds(ns) / ns, rounds = ceil(groups * ns / 256) (one
+    workgroup per CU of 256), ties to fewer splits, with at most two
+    workgroups per CU in all and at most one split per 128 keys (a 32-key tile
+    per wavefront); the permitted range is cut evenly."""
+    from fractions import Fraction
     elig = window if 0 < window < C else C
     units = B * hkv * -(-(hq // hkv) // 16)
-    ns = max(1, min(-(-512 // units), -(-elig // 128)))
+    max_ns = max(1, min(-(-elig // 128), 512 // units))
+    ns = min(range(1, max_ns + 1), key=lambda c: (Fraction(-(-units * c // 256), c), c))
     chunk = max(128, -(-elig // ns))
     nsplit = -(-elig // chunk) if elig > 0 else 0
     rows = B * hq * nsplit
@@ -232,5 +236,9 @@ def test_decode_plan_even_chunks():
         assert L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, 1) == want, (B, C, hq, hkv, d, w)
         elig = w if 0 < w < C else C
         assert chunk >= 128 and (nsplit - 1) * chunk < elig <= nsplit * chunk
-    # the headline decode: 8 chunks of 1000 keys, not 7 of 1024 and one of 832
-    assert _decode_plan_bytes(8, 8000, 32, 8, 128, -1)[1:] == (8, 1000)
+    # the headline decode: 4 chunks of 2000 keys for 64 groups, one
+    # workgroup per CU; 16 groups (the MQA endpoint) take 16 splits
+    assert _decode_plan_bytes(8, 8000, 32, 8, 128, -1)[1:] == (4, 2000)
+    assert _decode_plan_bytes(16, 8000, 8, 1, 128, -1)[1:] == (16, 500)
+    # 129 groups: 3 splits (387 workgroups, 2 rounds) beat 1 or 2 (1 or 2 rounds of a full range)
+    assert _decode_plan_bytes(129, 4000, 4, 1, 64, -1)[1] == 3
