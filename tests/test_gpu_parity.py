@@ -209,6 +209,26 @@ def test_decode_generic_sweep(dtype, d):
             assert np.array_equal(_np(rec).astype(np.int32), rrec)
 
 
+@pytest.mark.parametrize("B,C,hq,hkv,d,window", [
+    (129, 600, 4, 1, 64, None),    # 129 groups: 3 splits, 387 workgroups in 2 rounds
+    (600, 200, 4, 1, 64, None),    # 600 groups: no split, 600 workgroups
+    (24, 3000, 8, 1, 128, 700),    # 24 groups, window 700: 6 splits of 128 keys
+    (3, 5000, 64, 2, 64, None),    # two head chunks per KV group, 12 groups: 21 splits of 239 keys
+])
+def test_decode_split_plan_grids(B, C, hq, hkv, d, window):
+    # the split plan's less common grids: several rounds of workgroups, no
+    # split at all, short uneven chunks, and two head chunks per KV group
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 900 + B, DEV)
+    rng = np.random.default_rng(B)
+    seqlens = rng.integers(0, C + 1, size=B).tolist()
+    seqlens[0] = C
+    out, rec = run_decode(q, k, v, seqlens=seqlens, window=window, records=True)
+    ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=seqlens, window=window,
+                                 want_records=True)
+    assert _maxerr(_np(out), ref) <= BF16_TOL
+    assert np.array_equal(_np(rec).astype(np.int32), rrec)
+
+
 def test_decode_equals_prefill_row():
     # the full/cached invariant on the device: decode at n equals prefill row n-1
     B, hq, hkv, T, d = 2, 8, 2, 150, 128
