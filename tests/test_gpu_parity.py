@@ -428,3 +428,37 @@ def test_full_prefill_t4096_sampled_rows():
     for tt in (0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 4094, 4095):
         ref, _, _ = oracle.decode(_np(q[:, :, tt]), kn, vn, seqlens=[tt + 1])
         assert _maxerr(o[:, tt], ref) <= BF16_TOL, tt
+
+
+def test_offsets_beyond_2_31_elements():
+    # K/V of 2 * (2^24 + 5) * 128 elements each (8.6 GB): the rows below
+    # read only cells near the end of the second sequence, about 2^32
+    # elements into the tensors, so every K/V offset is a 64-bit one.  Only
+    # the read cells hold data; the oracle sees that slice.
+    B, hkv, hq, d, C = 2, 1, 4, 128, (1 << 24) + 5
+    tail = 300
+    assert (B - 1) * C * d > 2 ** 31
+    k = torch.zeros((B, hkv, C, d), dtype=torch.bfloat16, device=DEV)
+    v = torch.zeros_like(k)
+    k[:, :, C - tail:] = synth.randn((B, hkv, tail, d), 7001, torch.bfloat16, DEV)
+    v[:, :, C - tail:] = synth.randn((B, hkv, tail, d), 7002, torch.bfloat16, DEV)
+    ks, vs = _np(k[:, :, C - tail:]), _np(v[:, :, C - tail:])
+    # decode: window 100 at n_b = C reads cells C-100 .. C-1
+    q = synth.randn((B, hq, d), 7003, torch.bfloat16, DEV)
+    out, rec = run_decode(q, k, v, seqlens=[C, C], window=100, records=True)
+    ref, _, rrec = oracle.decode(_np(q), ks, vs, seqlens=[tail, tail], window=100, want_records=True)
+    assert _maxerr(_np(out), ref) <= BF16_TOL
+    r = _np(rec).astype(np.int64)
+    assert np.array_equal(r[..., 0], rrec[..., 0])
+    assert np.array_equal(r[..., 1:3], rrec[..., 1:3].astype(np.int64) + (C - tail))  # shifted cells
+    assert np.array_equal(r[..., 3], rrec[..., 3])
+    # prefix rows: the last 64 cells as new rows, window 200
+    Tq = 64
+    qp = synth.randn((B, hq, Tq, d), 7004, torch.bfloat16, DEV)
+    outp = gqa.prefill_prefix(qp, k, v, seqlens=[C, C], qlens=[Tq, Tq], window=200)
+    torch.cuda.synchronize()
+    refp, _, _ = oracle.attend_prefix(_np(qp), ks, vs, seqlens=[tail, tail], qlens=[Tq, Tq],
+                                      window=200)
+    assert _maxerr(_np(outp), refp) <= BF16_TOL
+    del k, v
+    torch.cuda.empty_cache()
