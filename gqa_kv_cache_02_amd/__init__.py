@@ -150,6 +150,9 @@ def _ptr(t):
 def _check_tensor(name, t, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        # the library takes device pointers only; host memory is never passed on
+        raise ValueError(f"{name} is on {t.device}; the kernels need GPU tensors")
     if t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:

@@ -242,3 +242,19 @@ def test_decode_plan_even_chunks():
     assert _decode_plan_bytes(16, 8000, 8, 1, 128, -1)[1:] == (16, 500)
     # 129 groups: 3 splits (387 workgroups, 2 rounds) beat 1 or 2 (1 or 2 rounds of a full range)
     assert _decode_plan_bytes(129, 4000, 4, 1, 64, -1)[1] == 3
+
+
+def test_binding_refuses_host_tensors():
+    """The binding passes device pointers only: CPU tensors are refused in
+    Python, before any library call (no CPU path exists to fall back to)."""
+    import torch
+    q = torch.zeros((1, 4, 4, 8), dtype=torch.float32)
+    k = torch.zeros((1, 2, 4, 8), dtype=torch.float32)
+    with pytest.raises(ValueError, match="GPU tensors"):
+        gqa.prefill(q, k, k.clone())
+    with pytest.raises(ValueError, match="GPU tensors"):
+        gqa.decode(q[:, :, 0].contiguous(), k, k.clone())
+    with pytest.raises(ValueError, match="GPU tensors"):
+        gqa.prefill_prefix(q, k, k.clone())
+    with pytest.raises(ValueError, match="GPU tensors"):
+        gqa.decode_cache(q[:, :, 0].contiguous(), k, k.clone())
