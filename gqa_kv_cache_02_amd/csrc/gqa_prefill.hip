@@ -5,12 +5,13 @@
 // matrix; the dense pairwise work remains).
 //
 // Work decomposition.  A workgroup owns one batch row b, one KV group g and
-// one block of query rows, and runs up to 4 wavefronts: `hpw` query heads of
-// group g times `rb` blocks of 32 rows (hpw * rb <= 4).  All its wavefronts
-// read the same K/V tiles, which are staged once in LDS per workgroup -- the
-// r query heads that share a KV head ("Share key/value heads and make context
-// explicit", "Give each query head an explicit shared KV head") never cause a
-// second read or a repeated copy.
+// one block of query rows, and runs 8 wavefronts (one workgroup per CU, two
+// wavefronts per SIMD): `hpw` query heads of group g times `rb` blocks of 32
+// rows (hpw * rb = 8).  All its wavefronts read the same K/V tiles, which are
+// staged once in LDS per workgroup -- the r query heads that share a KV head
+// ("Share key/value heads and make context explicit", "Give each query head
+// an explicit shared KV head") never cause a second read or a repeated copy,
+// and one staged tile feeds 8 wavefronts.
 //
 // Per 64-key tile and wavefront (32 query rows):
 //   S^T[64 keys x 32 rows] = K[64 x d] . Q^T[d x 32]     (MFMA 32x32x16 bf16)
@@ -35,6 +36,7 @@ namespace gqa {
 
 constexpr int kPBN = 64;   // keys per K/V tile
 constexpr int kPRows = 32; // query rows per wavefront
+constexpr int kPWaves = 8; // wavefronts per workgroup
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
@@ -275,14 +277,14 @@ template <int D, bool kRecord> struct TileMath {
 };
 
 template <int D, bool kRecord>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a) {
     using L = PrefillLayout<D>;
     using TM = TileMath<D, kRecord>;
     constexpr int KS = D / 16;   // 16-feature k-steps of Q.K (32x32x16)
     constexpr int DB = D / 32;   // 32-column blocks of P.V
     constexpr int CPR = L::CPR;
-    constexpr int NLD = CPR / 4; // 1 KiB direct loads per wavefront per tensor per tile
+    constexpr int NLD = CPR / kPWaves; // 1 KiB direct loads per wavefront per tensor per tile
 
     // Two stages of [K | V] tiles.  Separate objects (and a loop unrolled by
     // two) let the compiler see that reads of one stage never alias the
@@ -348,7 +350,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int w_lo_last = wave_max_i(row_on ? lo_row : -1);
     const int w_last = wave_max_i(row_on ? my_pos : -1);        // -1: no active row
     const int w_first = wave_min_i(row_on ? my_pos : INT_MAX);
-    __shared__ int sm_range[4][2];
+    __shared__ int sm_range[kPWaves][2];
     if (lane == 0) {
         sm_range[wave][0] = w_lo;
         sm_range[wave][1] = w_last;
@@ -356,7 +358,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     __syncthreads();
     int wg_lo = INT_MAX, wg_last = -1;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kPWaves; ++w) {
         wg_lo = min(wg_lo, sm_range[w][0]);
         wg_last = max(wg_last, sm_range[w][1]);
     }
@@ -449,7 +451,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const uint16_t *vbase = a.v + kv_off;
 
     // Direct loads of one tile into a stage: wavefront w issues loads
-    // ii = it*4 + w; lane l fills linear chunk ii*64 + l, i.e. row
+    // ii = it*8 + w; lane l fills linear chunk ii*64 + l, i.e. row
     // (ii*64 + l) / CPR and slot (ii*64 + l) % CPR, with the global chunk the
     // swizzle puts there.  An interior tile uses per-lane byte offsets fixed
     // for the whole loop; the workgroup's last tile repeats its last key in
@@ -457,7 +459,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     uint32_t koffs[NLD], voffs[NLD];
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
-        const int ii = it * 4 + wave_u;
+        const int ii = it * kPWaves + wave_u;
         const int lin = ii * 64 + lane;
         const int row = lin / CPR;
         const int slot = lin % CPR;
@@ -471,14 +473,14 @@ void prefill_mfma_kernel(PrefillArgs a) {
             const void *vb0 = vbase + (int64_t)j0 * D;
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
-                const int ii = it * 4 + wave_u;
+                const int ii = it * kPWaves + wave_u;
                 dma16s(kb0, koffs[it], dst + ii * 1024);
                 dma16s(vb0, voffs[it], dst + L::kTileBytes + ii * 1024);
             }
         } else {
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
-                const int ii = it * 4 + wave_u;
+                const int ii = it * kPWaves + wave_u;
                 const int lin = ii * 64 + lane;
                 const int row = lin / CPR;
                 const int slot = lin % CPR;
@@ -647,21 +649,21 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefillArgs a) {
     }
 }
 
-// Heads per workgroup: the largest divisor of r that is at most 4; the
-// remaining wavefronts take further 32-row blocks of the same heads.
+// Heads per workgroup: the largest power of two (at most 8) that divides r;
+// the remaining wavefronts take further 32-row blocks of the same heads, so
+// every workgroup runs all 8 wavefronts.  (One staged tile feeds 8
+// wavefronts whatever the split between heads and rows; more heads mean
+// fewer rows per workgroup and less work on the causal diagonal.)
 static void prefill_shape(int r, int *hpw, int *rb) {
-    int best = 1;
-    for (int x = 4; x >= 1; --x)
-        if (r % x == 0) {
-            best = x;
-            break;
-        }
-    *hpw = best;
-    *rb = (4 % best == 0) ? 4 / best : 1;
+    int x = kPWaves;
+    while (r % x != 0)
+        x /= 2;
+    *hpw = x;
+    *rb = kPWaves / x;
 }
 
 // The grid is one-dimensional: ceil(T / (32*rb)) * B * Hkv * (r/hpw)
-// workgroups of 256 work-items, whose total must fit a 32-bit count.
+// workgroups of 512 work-items, whose total must fit a 32-bit count.
 static int64_t prefill_workgroups(int B, int T, int Hq, int Hkv) {
     int hpw, rb;
     prefill_shape(Hq / Hkv, &hpw, &rb);
@@ -671,15 +673,15 @@ static int64_t prefill_workgroups(int B, int T, int Hq, int Hkv) {
 
 bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit) {
     const int64_t wgs = prefill_workgroups(B, T, Hq, Hkv) * (nsplit > 1 ? nsplit : 1);
-    return T >= 0 && wgs * 256 <= (int64_t)UINT32_MAX &&
+    return T >= 0 && wgs * kPWaves * 64 <= (int64_t)UINT32_MAX &&
            (int64_t)B * T * Hq * 64 <= (int64_t)UINT32_MAX; // merge grid
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Split of the key range for queries against a cached prefix: when the
-// blocks alone give fewer than 512 workgroups (two per CU on 256 CUs), each
-// block's key range is cut into nsplit parts of tps tiles (at least 4).  The
+// blocks alone give fewer than 256 workgroups (one per CU), each block's key
+// range is cut into nsplit parts of tps tiles (at least 4).  The
 // plan depends only on the arguments (the workspace size is a function of
 // them).
 PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window) {
@@ -694,7 +696,7 @@ PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window) 
     // tiles a block can span: its rows' key ranges, at most the cache
     const int64_t maxtiles = std::min<int64_t>((C + kPBN - 1) / kPBN,
                                                (elig + kPRows * rb) / kPBN + 2);
-    const int64_t target = 512;
+    const int64_t target = 256;
     if (units > 0 && units < target && maxtiles >= 8) {
         int64_t ns = (target + units - 1) / units;
         ns = std::min<int64_t>(ns, maxtiles / 4);
@@ -715,7 +717,7 @@ PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window) 
 
 template <int D, bool kRecord>
 static hipError_t launch_p(const PrefillArgs &a, dim3 grid, hipStream_t s) {
-    prefill_mfma_kernel<D, kRecord><<<grid, 256, 0, s>>>(a);
+    prefill_mfma_kernel<D, kRecord><<<grid, kPWaves * 64, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit <= 1)
         return e;
