@@ -78,7 +78,10 @@ template <int D> struct DecodeSmem {
     // with ds_read_b64_tr_b16 on disjoint banks.
     static constexpr int LDV = D + 16;
     static constexpr int kVBytes = kDecodeWaves * kDecodeTile * LDV * 2;
-    static constexpr int kOBytes = kDecodeWaves * kDecodeHeads * D * 4;
+    // Staged partial outputs: rows of D + 4 floats, so that the 16 heads'
+    // 16-byte writes fall on distinct banks.
+    static constexpr int LDO = D + 4;
+    static constexpr int kOBytes = kDecodeWaves * kDecodeHeads * LDO * 4;
     static constexpr int kBytes = (kVBytes > kOBytes ? kVBytes : kOBytes);
 };
 
@@ -92,6 +95,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int KS = D / 32;               // 32-feature k-steps of Q.K
     constexpr int DB = D / 16;               // 16-column blocks of P.V
     constexpr int LDV = DecodeSmem<D>::LDV;
+    constexpr int LDO = DecodeSmem<D>::LDO;
     constexpr int VPI = 1024 / (2 * D);      // keys per 1 KiB wavefront load
     constexpr int LPK = 64 / VPI;            // lanes per key row
     constexpr int VIT = kDecodeTile / VPI;   // V loads per tile
@@ -100,6 +104,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[DecodeSmem<D>::kBytes];
     __shared__ float sm_m[kDecodeWaves][kDecodeHeads];
     __shared__ float sm_l[kDecodeWaves][kDecodeHeads];
+    __shared__ float sm_lse[kDecodeHeads];
     __shared__ int sm_rec[kDecodeWaves][4];
 
     const int tid = threadIdx.x;
@@ -392,7 +397,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
     }
 
-    // Merge the 4 wavefronts of the workgroup.
+    // Merge the 4 wavefronts of the workgroup.  Each wavefront weights its
+    // partial by 2^(m_w - max m) / sum_w' 2^(m_w' - max m) l_w', so that the
+    // workgroup's normalised result is the plain sum of the 4 weighted
+    // partials; only the group's nh real heads are staged.
     if (qg == 0) {
         sm_m[wave][hl] = m;
         sm_l[wave][hl] = lsum;
@@ -402,13 +410,21 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 #pragma unroll
     for (int w = 0; w < kDecodeWaves; ++w)
         mx = fmaxf(mx, sm_m[w][hl]);
-    const float my_scale = fast_exp2(m - mx);
+    float tot = 0.f; // > 0: wavefront 0 folded at least key c_lo
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w)
+        tot += fast_exp2(sm_m[w][hl] - mx) * sm_l[w][hl];
+    const float my_w = fast_exp2(m - mx) / tot; // 0 for a wavefront that folded no key
+    if (wave == 0 && qg == 0)
+        sm_lse[hl] = mx + __builtin_amdgcn_logf(tot); // log2-sum-exp of the chunk
     float *os = reinterpret_cast<float *>(smem);
+    if (hl < nh) {
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            os[(wave * kDecodeHeads + hl) * D + db * 16 + qg * 4 + i] = oacc[db][i] * my_scale;
+        for (int db = 0; db < DB; ++db)
+            *reinterpret_cast<float4 *>(os + (wave * kDecodeHeads + hl) * LDO + db * 16 + qg * 4) =
+                make_float4(oacc[db][0] * my_w, oacc[db][1] * my_w, oacc[db][2] * my_w,
+                            oacc[db][3] * my_w);
+    }
     __syncthreads();
 
     int rec_cnt = 0, rec_lo = INT_MAX, rec_hi = -1, rec_xor = 0;
@@ -422,28 +438,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         }
     }
 
-    for (int idx = tid; idx < kDecodeHeads * D; idx += 256) {
-        const int h = idx / D;
-        const int c = idx % D;
-        if (h >= nh)
-            break;
-        float hm = -INFINITY;
+    // 4 output features per work-item.
+    for (int idx = tid; idx < nh * (D / 4); idx += 256) {
+        const int h = idx / (D / 4);
+        const int c = (idx % (D / 4)) * 4;
+        float4 o = *reinterpret_cast<const float4 *>(os + h * LDO + c);
 #pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w)
-            hm = fmaxf(hm, sm_m[w][h]);
-        float hl_sum = 0.f, o = 0.f;
-#pragma unroll
-        for (int w = 0; w < kDecodeWaves; ++w) {
-            hl_sum += fast_exp2(sm_m[w][h] - hm) * sm_l[w][h];
-            o += os[(w * kDecodeHeads + h) * D + c];
+        for (int w = 1; w < kDecodeWaves; ++w) {
+            const float4 t = *reinterpret_cast<const float4 *>(os + (w * kDecodeHeads + h) * LDO + c);
+            o.x += t.x;
+            o.y += t.y;
+            o.z += t.z;
+            o.w += t.w;
         }
         if (ns == 1) {
             // the whole row was this chunk: finished
-            a.out[(row0 + h) * D + c] = f32_to_bf16(o / hl_sum);
+            uint2 pk;
+            pk.x = pack_bf16x2(o.x, o.y);
+            pk.y = pack_bf16x2(o.z, o.w);
+            *reinterpret_cast<uint2 *>(a.out + (row0 + h) * D + c) = pk;
         } else {
-            a.o_part[((row0 + h) * a.nsplit + split) * D + c] = o / hl_sum;
+            *reinterpret_cast<float4 *>(a.o_part + ((row0 + h) * a.nsplit + split) * D + c) = o;
             if (c == 0)
-                a.lse_part[(row0 + h) * a.nsplit + split] = hm + __builtin_amdgcn_logf(hl_sum);
+                a.lse_part[(row0 + h) * a.nsplit + split] = sm_lse[h];
         }
     }
     if (kRecord && tid < nh) {
