@@ -129,10 +129,12 @@ def test_prefill_sweep(dtype, d):
 @pytest.mark.parametrize("d", [64, 128])
 def test_prefill_mfma_sweep(d):
     # several 64-key tiles, ragged active lengths, windows crossing tile
-    # edges, and every heads-per-workgroup shape (r = 1, 2, 3, 4, 6, 8)
+    # edges, and every heads-per-workgroup shape of the 8-wavefront
+    # workgroups: r = 1, 3, 5 (1 head x 8 row blocks; 1, 3, 5 head chunks),
+    # 2, 6 (2 x 4), 4, 12 (4 x 2), 8, 16 (8 heads x 1 block; 1, 2 chunks)
     B, T, C = 3, 300, 333
     seqlens = [300, 129, 1]
-    for hq, hkv in ((4, 4), (4, 2), (6, 2), (8, 2), (12, 2), (16, 2)):
+    for hq, hkv in ((4, 4), (4, 2), (6, 2), (8, 2), (10, 2), (12, 2), (16, 2), (24, 2), (32, 2)):
         assert gqa.prefill_kernel(B, T, C, hq, hkv, d) == "prefill_mfma"
         q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, 900 + d + hq, DEV, C=C)
         for w in (None, 1, 33, 63, 64, 65, 100):
