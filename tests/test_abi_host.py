@@ -258,3 +258,21 @@ def test_binding_refuses_host_tensors():
         gqa.prefill_prefix(q, k, k.clone())
     with pytest.raises(ValueError, match="GPU tensors"):
         gqa.decode_cache(q[:, :, 0].contiguous(), k, k.clone())
+
+
+def _native_check():
+    import __graft_entry__ as entry
+    if not os.path.exists(entry.NATIVE_BIN):
+        entry.build_native_check()
+    return entry.NATIVE_BIN
+
+
+def test_native_program_refusals():
+    """The C ABI from native code (tests/native/abi_check.cpp, no Python in
+    the call path): refusals come back before any launch and the host helpers
+    reproduce the pages' tables."""
+    import subprocess
+    res = subprocess.run([_native_check(), "refusals"], capture_output=True, text=True,
+                         timeout=60)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip() == "refusals ok"
