@@ -136,3 +136,31 @@ def test_negative_and_zero_scale(d):
             mean = (cs[:, t + 1] - cs[:, lo]) / (t + 1 - lo)  # [Hkv, d]
             want = np.repeat(mean, hq // hkv, axis=0)
             assert np.abs(o[b, t] - want).max() <= TOL, (b, t)
+
+
+@pytest.mark.parametrize("d", [8, 200])
+@pytest.mark.parametrize("rate", [0.2, -0.2])
+def test_moving_maximum_generic_fp32(d, rate):
+    # the generic kernel (fp32 storage, any d) has its own online softmax; its
+    # maximum moves on every key here.  fp32 rounds a score s to about
+    # |s| * 2^-24 per term, so against 1e-5 the scores stay near 100 or below
+    # (at rate 0.7 they reach ~410 and the rounding alone moves the output
+    # by ~1e-5).
+    B, T, hq, hkv = 2, 300, 6, 2
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.float32, 6300 + d, "cpu")
+    q, k = q * 0.05, k * 0.05
+    scale = 1.0 / np.sqrt(d)
+    q[..., 0] = 4.0
+    k[..., 0] = torch.arange(T, dtype=torch.float32) * (rate / (4.0 * scale * LOG2E))
+    q, k, v = q.to(DEV), k.to(DEV), v.to(DEV)
+    seqlens = [300, 123]
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    for w in (None, 77):
+        assert gqa.prefill_kernel(B, T, T, hq, hkv, d, w, torch.float32) == "generic"
+        out = gqa.prefill(q, k, v, seqlens=sl, window=w)
+        dout = gqa.decode(q[:, :, T - 1].contiguous(), k, v, window=w)
+        torch.cuda.synchronize()
+        ref, _, _ = oracle.prefill(_np(q), _np(k), _np(v), seqlens=seqlens, window=w)
+        dref, _, _ = oracle.decode(_np(q[:, :, T - 1]), _np(k), _np(v), window=w)
+        assert float(np.max(np.abs(_np(out) - ref))) <= 1e-5, ("prefill", d, rate, w)
+        assert float(np.max(np.abs(_np(dout) - dref))) <= 1e-5, ("decode", d, rate, w)
