@@ -264,6 +264,14 @@ def test_full_chunked_prefill_t512_c4096():
     B, Tq, C, hq, hkv, d = cfg["B"], cfg["Tq"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"]
     q, k, v = synth.prefill_inputs(B, Tq, hq, hkv, d, torch.bfloat16, cfg["seed"], DEV, C=C)
     out, rec = run_prefix(q, k, v, [C], [Tq], None, None)
+    # the instantiation bench.py times (no records), called as it calls it:
+    # bit for bit the output of the record-writing one
+    ws = torch.empty(max(1, gqa.prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d)),
+                     dtype=torch.uint8, device=DEV)
+    plain = torch.empty_like(out)
+    gqa.prefill_prefix(q, k, v, out=plain, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, out)
     r = _np(rec).astype(np.int64)
     p = (C - Tq + np.arange(Tq))[None, :, None]
     assert (r[..., 1] == 0).all() and (r[..., 2] == p).all() and (r[..., 3] == p + 1).all()
@@ -284,6 +292,14 @@ def test_full_ring_decode_ragged_w4096():
     kn, vn = _cand(B, hkv, d, torch.bfloat16, cfg["seed"] + 50)
     k0, v0 = k.clone(), v.clone()
     out, rec = run_cache(q, k, v, kn, vn, seqlens, w, True)
+    # the instantiation bench.py times (no records) on a second copy of the
+    # original cache: the same output bit for bit and the same committed cache
+    k2, v2 = k0.clone(), v0.clone()
+    plain = gqa.decode_cache(q, k2, v2, k_new=kn, v_new=vn,
+                             seqlens=torch.tensor(seqlens, dtype=torch.int32, device=DEV),
+                             window=w, ring=True)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, out) and torch.equal(k2, k) and torch.equal(v2, v)
     _, _, _, rrec = oracle.decode_cache(np.zeros((B, hq, 1)), np.zeros((B, hkv, C, 1)),
                                         np.zeros((B, hkv, C, 1)), seqlens=seqlens, window=w,
                                         ring=True, want_records=True)

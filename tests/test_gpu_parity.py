@@ -371,6 +371,15 @@ def _decode_full_check(B, C, hq, hkv, d, seqlens, window, seed, sample_b):
     lo = [0 if window is None else max(0, n - window) for n in seqlens]
     hi = [n - 1 for n in seqlens]
     assert _convex_bounds_ok(out, v, hq, hkv, lo, hi)
+    # the instantiation bench.py times (no records), called as it calls it:
+    # bit for bit the output of the record-writing one above
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, C, hq, hkv, d, window)),
+                     dtype=torch.uint8, device=DEV)
+    plain = torch.empty_like(out)
+    gqa.decode(q, k, v, seqlens=sl, window=window, out=plain, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, out)
 
 
 def test_full_decode_b8_hq32_hkv8_d128_n8000():
@@ -420,6 +429,11 @@ def test_full_prefill_t4096_sampled_rows():
     out, rec = run_prefill(q, k, v, records=True)
     o = _np(out)
     assert np.isfinite(o).all()
+    # the instantiation bench.py times (no records), called as it calls it
+    plain = torch.empty_like(out)
+    gqa.prefill(q, k, v, out=plain)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, out)
     r = _np(rec).astype(np.int64)
     t = np.arange(T)[None, :, None]
     h = np.arange(hq)[None, None, :]
