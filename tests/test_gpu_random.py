@@ -5,7 +5,9 @@ prefix, decode with a committed candidate or over a rolling cache), dtype,
 head counts (group sizes 1 to 16, powers of two and not), head width, batch, capacity, ragged
 lengths and window from a fixed seed, so a failure names a reproducible
 case.  Tolerances as in test_gpu_parity: max-abs 1e-5 (fp32 storage) and
-2e-2 (bf16 storage); index-set records and committed cache cells exact.
+2e-2 (bf16 storage); index-set records and committed cache cells exact.  Every
+case also runs the record-free instantiation, which must give the same output
+(and committed caches) bit for bit.
 """
 import numpy as np
 import pytest
@@ -84,7 +86,9 @@ def test_random_case(case):
         q, k, v = synth.decode_inputs(B, C, hq, hkv, d, dtype, seed, DEV)
         rec = torch.full((B, hq, 5), -7, dtype=torch.int32, device=DEV)
         out = gqa.decode(q, k, v, seqlens=_i32(seqlens), window=w, records=rec)
+        plain = gqa.decode(q, k, v, seqlens=_i32(seqlens), window=w)
         torch.cuda.synchronize()
+        assert torch.equal(plain, out), what
         ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
                                      want_records=True)
         assert _maxerr(_np(out), ref) <= tol, what
@@ -98,7 +102,9 @@ def test_random_case(case):
         q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, dtype, seed, DEV, C=C)
         rec = torch.full((B, T, hq, 5), -7, dtype=torch.int32, device=DEV)
         out = gqa.prefill(q, k, v, seqlens=_i32(seqlens), window=w, records=rec)
+        plain = gqa.prefill(q, k, v, seqlens=_i32(seqlens), window=w)
         torch.cuda.synchronize()
+        assert torch.equal(plain, out), what
         ref, _, rrec = oracle.prefill(_np(q), _np(k), _np(v), seqlens=seqlens, window=w,
                                       want_records=True)
         assert _maxerr(_np(out), ref) <= tol, what
@@ -126,7 +132,10 @@ def test_random_case(case):
         out = gqa.prefill_prefix(q, k, v, seqlens=_i32(seqlens), qlens=_i32(qlens),
                                  seg_starts=None if segs is None else _i32(segs), window=w,
                                  records=rec)
+        plain = gqa.prefill_prefix(q, k, v, seqlens=_i32(seqlens), qlens=_i32(qlens),
+                                   seg_starts=None if segs is None else _i32(segs), window=w)
         torch.cuda.synchronize()
+        assert torch.equal(plain, out), what
         ref, _, rrec = oracle.attend_prefix(_np(q), _np(k), _np(v), seqlens=seqlens,
                                             qlens=qlens, segs=segs, window=w,
                                             want_records=True)
@@ -148,10 +157,14 @@ def test_random_case(case):
             kn = synth.randn((B, hkv, d), seed + 50, dtype, DEV)
             vn = synth.randn((B, hkv, d), seed + 51, dtype, DEV)
         k0, v0 = _np(k), _np(v)
+        kc, vc = k.clone(), v.clone()
         rec = torch.full((B, hq, 5), -7, dtype=torch.int32, device=DEV)
         out = gqa.decode_cache(q, k, v, k_new=kn, v_new=vn, seqlens=_i32(seqlens), window=w,
                                ring=ring, records=rec)
+        plain = gqa.decode_cache(q, kc, vc, k_new=kn, v_new=vn, seqlens=_i32(seqlens), window=w,
+                                 ring=ring)
         torch.cuda.synchronize()
+        assert torch.equal(plain, out) and torch.equal(kc, k) and torch.equal(vc, v), what
         ref, rk, rv, rrec = oracle.decode_cache(
             _np(q), k0, v0, None if kn is None else _np(kn), None if vn is None else _np(vn),
             seqlens=seqlens, window=w, ring=ring, want_records=True)
