@@ -15,3 +15,14 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="session", autouse=True)
+def _built_library():
+    """libgqa.so is built in-tree by __graft_entry__.build().  A checkout with
+    nothing built gets it built here, once (hipcc cross-compiles for gfx950
+    without a GPU); an existing build is used as it is."""
+    lib = os.path.join(ROOT, "gqa_kv_cache_02_amd", "libgqa.so")
+    if not os.path.exists(lib):
+        from gqa_kv_cache_02_amd import build
+        build.build()
