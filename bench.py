@@ -24,7 +24,10 @@ Prints ONE JSON line.
                  device copy; frac_of_measured_copy is `value` against it.
   prefill        causal prefill B=1, T=4096, Hq=32, Hkv=8, d=128: TFLOP/s of
                  the permitted pairs (4*d flops each) against 2.5 PFLOP/s
-                 dense bf16 MFMA.
+                 dense bf16 MFMA; `mfma_counters` carries the matrix-core busy
+                 fraction, clock and executed MFMA work that rocprofv3
+                 counters measured (profiles/), while the kernel source still
+                 has the hash they were taken with.
   prefix_prefill queries against a cached prefix: the last 512 cells of a
                  4096-cell sequence as new rows (B=1, Hq=32, Hkv=8, d=128):
                  TFLOP/s of the permitted pairs against 2.5 PFLOP/s.
@@ -60,6 +63,8 @@ BF16_PEAK_TFLOPS = 2500.0
 COPY_CAL_BYTES = 1 << 30  # plain copy used to calibrate the traffic counters
 DECODE_SRC = os.path.join(ROOT, "gqa_kv_cache_02_amd", "csrc", "gqa_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b8_hq32_hkv8_d128_n8000_traffic.txt")
+PREFILL_SRC = os.path.join(ROOT, "gqa_kv_cache_02_amd", "csrc", "gqa_prefill.hip")
+MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_b1_t4096_hq32_hkv8_d128_mfma_counters.txt")
 
 
 def decode_bytes(B, Hq, Hkv, d, cells, elem=2):
@@ -75,6 +80,29 @@ def prefill_flops(Hq, d, T, B=1):
 
 def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_mfma():
+    """Matrix-core counters of the causal prefill from the committed rocprofv3
+    summary (busy fraction of cycles at the clock the chip held, that clock,
+    executed MFMA work), or None when it is missing or was taken on a
+    different kernel source."""
+    if not os.path.exists(MFMA_FILE):
+        return None
+    vals = {}
+    for ln in open(MFMA_FILE):
+        if "=" in ln and not ln.lstrip().startswith("#"):
+            k, v = ln.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("prefill_source_sha256_16") != source_hash(PREFILL_SRC):
+        return None
+    try:
+        return {"mfma_busy_frac": float(vals["mfma_busy_frac"]),
+                "sustained_clock_ghz": float(vals["sustained_clock_ghz"]),
+                "mfma_gflop_executed": float(vals["mfma_gflop_executed"]),
+                "source": "profiles/" + os.path.basename(MFMA_FILE)}
+    except (KeyError, ValueError):
+        return None
 
 
 def measured_traffic():
@@ -169,7 +197,8 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
                 flops=flops, tflops=round(tflops, 2),
                 frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
                 tokens_per_s=round(B * T / (ms * 1e-3), 1),
-                timing="HIP events on the launch stream around each call")
+                timing="HIP events on the launch stream around each call",
+                mfma_counters=measured_mfma())
 
 
 def _time_calls(torch, fn, steps, warmup):
