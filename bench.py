@@ -24,7 +24,8 @@ Prints ONE JSON line.
                  device copy; frac_of_measured_copy is `value` against it.
   prefill        causal prefill B=1, T=4096, Hq=32, Hkv=8, d=128: TFLOP/s of
                  the permitted pairs (4*d flops each) against 2.5 PFLOP/s
-                 dense bf16 MFMA; `mfma_counters` carries the matrix-core busy
+                 dense bf16 MFMA, over back-to-back calls (`per_call`: with
+                 events around each call); `mfma_counters` carries the matrix-core busy
                  fraction, clock and executed MFMA work that rocprofv3
                  counters measured (profiles/), while the kernel source still
                  has the hash they were taken with.
@@ -182,6 +183,16 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
     for _ in range(warmup):
         gqa.prefill(q, k, v, out=out)
     torch.cuda.synchronize()
+    # back-to-back calls between two events (as the decode `value`)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        gqa.prefill(q, k, v, out=out)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    # events around each call
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for i in range(steps):
         ev[2 * i].record()
@@ -189,15 +200,19 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
-    ms = sum(per) / steps
+    ms_call = sum(per) / steps
     flops = prefill_flops(hq, d, T, B)
     tflops = flops / (ms * 1e-3) / 1e12
+    tflops_call = flops / (ms_call * 1e-3) / 1e12
     return dict(workload="gqa_prefill_b1_t4096_hq32_hkv8_d128_causal_bf16",
                 kernel=gqa.prefill_kernel(B, T, T, hq, hkv, d), ms=round(ms, 5),
                 flops=flops, tflops=round(tflops, 2),
                 frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
                 tokens_per_s=round(B * T / (ms * 1e-3), 1),
-                timing="HIP events on the launch stream around each call",
+                timing="back-to-back calls between two HIP events on the launch stream",
+                per_call={"ms": round(ms_call, 5), "tflops": round(tflops_call, 2),
+                          "frac_of_bf16_peak": round(tflops_call / BF16_PEAK_TFLOPS, 4),
+                          "timing": "HIP events on the launch stream around each call"},
                 mfma_counters=measured_mfma())
 
 
