@@ -42,6 +42,10 @@ Prints ONE JSON line.
                  window 4096, linear cache: GB/s of the cells in the windows.
   small_f32_prefill  the fp32 prefill B=1, T=16, Hq=4, Hkv=2, d=8: us per
                  call (latency only), without a window and with window 2.
+  The prefix, rolling-cache, sweep and ragged legs time back-to-back calls
+  between two events, like `value`; `per_call_ms` adds events around each
+  call, which for calls shorter than the binding's host time per call
+  measures the host.
   cpu_baseline   the fp64 oracle (plain C, OpenMP) on the host cores, on the
                  same decode workload; with the CPU model, the process's
                  affinity set and a one-thread figure on one batch row.
@@ -216,10 +220,25 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
                 mfma_counters=measured_mfma())
 
 
+B2B = "back-to-back calls between two HIP events on the launch stream"
+PER_CALL = ("per_call_ms: HIP events on the launch stream around each call; it includes the "
+            "binding's host time when a call is shorter than that")
+
+
 def _time_calls(torch, fn, steps, warmup):
+    """(ms per call over `steps` back-to-back calls between two events,
+    mean ms with events around each call)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
     for i in range(steps):
         ev[2 * i].record()
@@ -227,7 +246,7 @@ def _time_calls(torch, fn, steps, warmup):
         ev[2 * i + 1].record()
     torch.cuda.synchronize()
     per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
-    return sum(per) / steps
+    return ms, sum(per) / steps
 
 
 def prefix_flops(Hq, d, C, Tq, B=1):
@@ -245,15 +264,15 @@ def bench_prefix(torch, gqa, synth, steps, warmup):
     out = torch.empty((B, Tq, hq, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, gqa.prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d)),
                      dtype=torch.uint8, device=dev)
-    ms = _time_calls(torch, lambda i: gqa.prefill_prefix(q, k, v, out=out, workspace=ws),
-                     steps, warmup)
+    ms, ms_call = _time_calls(torch, lambda i: gqa.prefill_prefix(q, k, v, out=out,
+                                                                  workspace=ws), steps, warmup)
     flops = prefix_flops(hq, d, C, Tq, B)
     tflops = flops / (ms * 1e-3) / 1e12
     return dict(workload="gqa_prefill_prefix_b1_tq512_c4096_hq32_hkv8_d128_bf16",
                 ms=round(ms, 5), flops=flops, tflops=round(tflops, 2),
                 frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
-                tokens_per_s=round(B * Tq / (ms * 1e-3), 1),
-                timing="HIP events on the launch stream around each call")
+                tokens_per_s=round(B * Tq / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5),
+                timing=f"{B2B}; {PER_CALL}")
 
 
 def bench_ring(torch, gqa, synth, steps, warmup):
@@ -277,7 +296,7 @@ def bench_ring(torch, gqa, synth, steps, warmup):
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, w, hq, hkv, d, w)), dtype=torch.uint8,
                      device=dev)
-    ms = _time_calls(torch, lambda i: gqa.decode_cache(q, ks[i % copies], vs[i % copies],
+    ms, ms_call = _time_calls(torch, lambda i: gqa.decode_cache(q, ks[i % copies], vs[i % copies],
                                                        k_new=kn, v_new=vn, seqlens=seqlens,
                                                        window=w, ring=True, out=out,
                                                        workspace=ws), steps, warmup)
@@ -288,7 +307,7 @@ def bench_ring(torch, gqa, synth, steps, warmup):
                 ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
                 frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
                 tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
-                timing="HIP events on the launch stream around each call")
+                per_call_ms=round(ms_call, 5), timing=f"{B2B}; {PER_CALL}")
 
 
 def bench_sweep(torch, gqa, synth, steps, warmup):
@@ -311,16 +330,16 @@ def bench_sweep(torch, gqa, synth, steps, warmup):
         out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
         ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, n, hq, hkv, d)), dtype=torch.uint8,
                          device=dev)
-        ms = _time_calls(torch, lambda i: gqa.decode(q, ks[i % copies], vs[i % copies], out=out,
+        ms, ms_call = _time_calls(torch, lambda i: gqa.decode(q, ks[i % copies], vs[i % copies], out=out,
                                                      workspace=ws), steps, warmup)
         nbytes = decode_bytes(B, hq, hkv, d, n)
         gbs = nbytes / (ms * 1e-3) / 1e9
         res.append(dict(Hkv=hkv, ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
                         frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
-                        tokens_per_s=round(B / (ms * 1e-3), 1)))
+                        tokens_per_s=round(B / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5)))
         del ks, vs, q, k0, v0
     return dict(workload="gqa_decode_sweep_b16_hq8_d128_n8000_bf16", results=res,
-                timing="HIP events on the launch stream around each call")
+                timing=f"{B2B}; {PER_CALL}")
 
 
 def bench_ragged_window(torch, gqa, synth, steps, warmup):
@@ -343,7 +362,7 @@ def bench_ragged_window(torch, gqa, synth, steps, warmup):
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, C, hq, hkv, d, w)), dtype=torch.uint8,
                      device=dev)
-    ms = _time_calls(torch, lambda i: gqa.decode(q, ks[i % copies], vs[i % copies],
+    ms, ms_call = _time_calls(torch, lambda i: gqa.decode(q, ks[i % copies], vs[i % copies],
                                                  seqlens=seqlens, window=w, out=out,
                                                  workspace=ws), steps, warmup)
     cells = int(sum(min(int(n), w) for n in lens.tolist()))
@@ -353,7 +372,7 @@ def bench_ragged_window(torch, gqa, synth, steps, warmup):
                 ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
                 frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
                 tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
-                timing="HIP events on the launch stream around each call")
+                per_call_ms=round(ms_call, 5), timing=f"{B2B}; {PER_CALL}")
 
 
 def bench_small_f32(torch, gqa, synth, steps, warmup):
@@ -366,8 +385,9 @@ def bench_small_f32(torch, gqa, synth, steps, warmup):
     out = torch.empty((B, T, hq, d), dtype=torch.float32, device=dev)
     res = {}
     for w in cfg["windows"]:
-        ms = _time_calls(torch, lambda i: gqa.prefill(q, k, v, window=w, out=out), steps, warmup)
-        res["no_window" if w is None else f"window_{w}"] = round(ms * 1e3, 2)
+        _, ms_call = _time_calls(torch, lambda i: gqa.prefill(q, k, v, window=w, out=out), steps,
+                                 warmup)
+        res["no_window" if w is None else f"window_{w}"] = round(ms_call * 1e3, 2)
     return dict(workload="gqa_prefill_b1_t16_hq4_hkv2_d8_causal_f32",
                 kernel=gqa.prefill_kernel(B, T, T, hq, hkv, d, dtype=torch.float32),
                 us_per_call=res, timing="HIP events on the launch stream around each call")

@@ -143,17 +143,20 @@ def _win(window) -> int:
     return GQA_NO_WINDOW if window is None else int(window)
 
 
+# The per-call checks below use the cheapest tensor queries (is_cuda,
+# get_device, plain integer pointers): a decode call on a small cache runs for
+# about as long as the Python side takes to issue it.
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _check_tensor(name, t, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         # the library takes device pointers only; host memory is never passed on
         raise ValueError(f"{name} is on {t.device}; the kernels need GPU tensors")
-    if t.device != device:
+    if t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if t.dtype != dtype:
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
@@ -161,8 +164,13 @@ def _check_tensor(name, t, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
 def _stream(device):
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    if _raw_stream is not None:
+        return _raw_stream(device.index)
+    return torch.cuda.current_stream(device).cuda_stream
 
 
 def _seq(seqlens, B, device):
@@ -237,8 +245,8 @@ def decode(q, k, v, *, seqlens=None, window=None, scale=None, out=None, workspac
     sl = _seq(seqlens, B, dev)
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     w = _win(window)
-    need = int(L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, _dt(q.dtype)))
     if workspace is None:
+        need = int(L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, _dt(q.dtype)))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, torch.uint8, dev)
     args = (_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sl), B, C, hq, hkv, d, w, sc,
@@ -301,9 +309,9 @@ def prefill_prefix(q, k, v, *, seqlens=None, qlens=None, seg_starts=None, window
         if records.shape != (B, Tq, hq, 5):
             raise ValueError("records must be int32 [B,Tq,Hq,5]")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    need = int(L.gqa_prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, _win(window),
-                                                    _dt(q.dtype)))
     if workspace is None:
+        need = int(L.gqa_prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, _win(window),
+                                                        _dt(q.dtype)))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, torch.uint8, dev)
     rc = L.gqa_prefill_prefix(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sl), _ptr(ql),
@@ -348,8 +356,8 @@ def decode_cache(q, k, v, *, k_new=None, v_new=None, seqlens=None, window=None, 
             raise ValueError("records must be int32 [B,Hq,5]")
     sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
     w = _win(window)
-    need = int(L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, _dt(q.dtype)))
     if workspace is None:
+        need = int(L.gqa_decode_workspace_bytes(B, C, hq, hkv, d, w, _dt(q.dtype)))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check_tensor("workspace", workspace, torch.uint8, dev)
     rc = L.gqa_decode_cache(_ptr(q), _ptr(k), _ptr(v), _ptr(k_new), _ptr(v_new), _ptr(out),
