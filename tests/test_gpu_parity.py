@@ -320,6 +320,25 @@ def test_refused_call_leaves_output_untouched():
     assert e.value.status == 6
     torch.cuda.synchronize()
     assert (outp == 5.0).all()
+    # a workspace shorter than the split plan needs: the binding passes the
+    # caller's workspace on unsized, and the library refuses it
+    tiny = torch.empty(1, dtype=torch.uint8, device=DEV)
+    q, k, v = synth.decode_inputs(2, 2000, 8, 2, 128, torch.bfloat16, 2, DEV)
+    assert gqa.decode_workspace_bytes(2, 2000, 8, 2, 128) > 1
+    out = torch.full((2, 8, 128), 3.0, dtype=torch.bfloat16, device=DEV)
+    for call in (lambda: gqa.decode(q, k, v, out=out, workspace=tiny),
+                 lambda: gqa.decode_cache(q, k, v, out=out, workspace=tiny)):
+        with pytest.raises(gqa.GQAError) as e:
+            call()
+        assert e.value.status == 8
+    qx, kx, vx = synth.prefill_inputs(1, 64, 8, 2, 128, torch.bfloat16, 3, DEV, C=2000)
+    assert gqa.prefill_prefix_workspace_bytes(1, 64, 2000, 8, 2, 128) > 1
+    outx = torch.full((1, 64, 8, 128), 5.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gqa.GQAError) as e:
+        gqa.prefill_prefix(qx, kx, vx, out=outx, workspace=tiny)
+    assert e.value.status == 8
+    torch.cuda.synchronize()
+    assert (out == 3.0).all() and (outx == 5.0).all()
 
 
 def test_empty_inputs():
