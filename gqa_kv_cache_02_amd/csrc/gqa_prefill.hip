@@ -604,24 +604,68 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefillArgs a) {
         return;
     const int64_t row = idx / Q4; // (b * T + i) * Hq + h
     const int c4 = static_cast<int>(idx % Q4) * 4;
+    // The partials are loaded kChunk splits at a time, every load of a chunk
+    // in flight together (a loop that waits on each load in turn makes the
+    // kernel a chain of memory round trips).  The first chunk's outputs stay
+    // in registers for the second pass.  A split with lse = -inf never wrote
+    // its output slot; that slot is loaded (it lies inside the workspace) but
+    // not used.  The arithmetic is the plain two-pass order: the maximum over
+    // all splits, then the weighted sums in split order.
+    constexpr int kChunk = 8;
+    const float *lse = a.lse_part + row;
+    const float *op = a.o_part + row * D + c4;
+    const int64_t ostride = rows * D;
+    float lc[kChunk];
+    float4 oc[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+        if (i < a.nsplit) {
+            lc[i] = lse[i * rows];
+            oc[i] = *reinterpret_cast<const float4 *>(op + i * ostride);
+        }
+    }
     float mx = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s)
-        mx = fmaxf(mx, a.lse_part[s * rows + row]);
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+        if (i < a.nsplit)
+            mx = fmaxf(mx, lc[i]);
+    for (int s0 = kChunk; s0 < a.nsplit; s0 += kChunk) {
+        float t[kChunk];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            if (s0 + i < a.nsplit)
+                t[i] = lse[(s0 + i) * rows];
+#pragma unroll
+        for (int i = 0; i < kChunk; ++i)
+            if (s0 + i < a.nsplit)
+                mx = fmaxf(mx, t[i]);
+    }
     uint2 pk = uint2{0u, 0u};
     if (mx != -INFINITY) {
         float den = 0.f;
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int s = 0; s < a.nsplit; ++s) {
-            const float l = a.lse_part[s * rows + row];
-            if (l == -INFINITY)
-                continue; // nothing folded (its partial output was never written)
-            const float w = fast_exp2(l - mx);
-            const float4 o = *reinterpret_cast<const float4 *>(a.o_part + (s * rows + row) * D + c4);
-            den += w;
-            acc.x = fmaf(w, o.x, acc.x);
-            acc.y = fmaf(w, o.y, acc.y);
-            acc.z = fmaf(w, o.z, acc.z);
-            acc.w = fmaf(w, o.w, acc.w);
+        for (int s0 = 0; s0 < a.nsplit; s0 += kChunk) {
+            if (s0 > 0) {
+#pragma unroll
+                for (int i = 0; i < kChunk; ++i) {
+                    if (s0 + i < a.nsplit) {
+                        lc[i] = lse[(s0 + i) * rows];
+                        oc[i] = *reinterpret_cast<const float4 *>(op + (s0 + i) * ostride);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                if (s0 + i >= a.nsplit || lc[i] == -INFINITY)
+                    continue; // past the last split, or nothing folded
+                const float w = fast_exp2(lc[i] - mx);
+                const float4 o = oc[i];
+                den += w;
+                acc.x = fmaf(w, o.x, acc.x);
+                acc.y = fmaf(w, o.y, acc.y);
+                acc.z = fmaf(w, o.z, acc.z);
+                acc.w = fmaf(w, o.w, acc.w);
+            }
         }
         const float inv = 1.f / den;
         pk.x = pack_bf16x2(acc.x * inv, acc.y * inv);
