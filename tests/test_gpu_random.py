@@ -9,6 +9,8 @@ case.  Tolerances as in test_gpu_parity: max-abs 1e-5 (fp32 storage) and
 case also runs the record-free instantiation, which must give the same output
 (and committed caches) bit for bit.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -20,7 +22,8 @@ from gqa_kv_cache_02_amd import synth
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-NCASES = 128
+# more cases for a longer run: GQA_RANDOM_CASES=2000 (case i uses seed i)
+NCASES = int(os.environ.get("GQA_RANDOM_CASES", "128"))
 
 
 def _np(t):
