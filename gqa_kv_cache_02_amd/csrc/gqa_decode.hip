@@ -557,13 +557,24 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
     pk.y = pack_bf16x2(acc.z * inv, acc.w * inv);
     *reinterpret_cast<uint2 *>(a.out + row * D + c4) = pk;
     if (kRecord && c4 == 0) {
+        // record partials: 16 bytes per split, kChunk splits in flight together
         int cnt = 0, x = 0, rl = INT_MAX, rh = -1;
-        for (int s = 0; s < ns; ++s) {
-            const int32_t *rp = a.rec_part + (row * a.nsplit + s) * 4;
-            cnt += rp[0];
-            rl = min(rl, rp[1]);
-            rh = max(rh, rp[2]);
-            x ^= rp[3];
+        const int4 *rp = reinterpret_cast<const int4 *>(a.rec_part) + row * a.nsplit;
+        for (int s0 = 0; s0 < ns; s0 += kChunk) {
+            int4 rc[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i)
+                if (s0 + i < ns)
+                    rc[i] = rp[s0 + i];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                if (s0 + i < ns) {
+                    cnt += rc[i].x;
+                    rl = min(rl, rc[i].y);
+                    rh = max(rh, rc[i].z);
+                    x ^= rc[i].w;
+                }
+            }
         }
         int32_t *rec = a.records + row * 5;
         rec[0] = static_cast<int>(row % a.Hq) / a.r;

@@ -673,15 +673,30 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefillArgs a) {
     }
     *reinterpret_cast<uint2 *>(a.out + row * D + c4) = pk;
     if (kRecord && c4 == 0) {
+        // record partials: 16 bytes per split, kChunk splits in flight
+        // together; a split with lse = -inf wrote none (its slot is loaded,
+        // inside the workspace, and skipped)
         int cnt = 0, x = 0, rl = INT_MAX, rh = -1;
-        for (int s = 0; s < a.nsplit; ++s) {
-            const int32_t *rp = a.rec_part + (s * rows + row) * 4;
-            if (a.lse_part[s * rows + row] == -INFINITY)
-                continue;
-            cnt += rp[0];
-            rl = min(rl, rp[1]);
-            rh = max(rh, rp[2]);
-            x ^= rp[3];
+        const int4 *rp = reinterpret_cast<const int4 *>(a.rec_part) + row;
+        for (int s0 = 0; s0 < a.nsplit; s0 += kChunk) {
+            int4 rc[kChunk];
+            float rlse[kChunk];
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                if (s0 + i < a.nsplit) {
+                    rc[i] = rp[(s0 + i) * rows];
+                    rlse[i] = lse[(s0 + i) * rows];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kChunk; ++i) {
+                if (s0 + i < a.nsplit && rlse[i] != -INFINITY) {
+                    cnt += rc[i].x;
+                    rl = min(rl, rc[i].y);
+                    rh = max(rh, rc[i].z);
+                    x ^= rc[i].w;
+                }
+            }
         }
         int32_t *rec = a.records + row * 5;
         rec[0] = static_cast<int>(row % a.Hq) / a.r;
