@@ -76,6 +76,10 @@ bool fast_shape(int32_t d, int32_t dtype) {
     return dtype == GQA_BF16 && (d == 64 || d == 128);
 }
 
+// The matrix-core kernels move 16 bytes per lane: q, k, v and out (and a
+// decode candidate) must be 16-byte aligned.  A call of their shape with a
+// pointer that is not is refused (GQA_ERR_ALIGN), never rerouted to another
+// kernel behind the caller's back.
 bool fast_aligned(const void *q, const void *k, const void *v, const void *out) {
     return aligned(q, 16) && aligned(k, 16) && aligned(v, 16) && aligned(out, 16);
 }
@@ -136,7 +140,9 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
     p.qlens = x.qlens;
     p.segs = x.segs;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (prefill_kernel_for(d, dtype) == GQA_KERNEL_PREFILL_MFMA && fast_aligned(q, k, v, out)) {
+    if (prefill_kernel_for(d, dtype) == GQA_KERNEL_PREFILL_MFMA) {
+        if (!fast_aligned(q, k, v, out))
+            return GQA_ERR_ALIGN;
         gqa::PrefixPlan plan{};
         plan.nsplit = 1;
         if (x.prefix)
@@ -197,18 +203,25 @@ int decode_impl(const void *q, const void *k, const void *v, void *out, const in
     p.ring = x.ring;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int r = Hq / Hkv;
-    const bool cand_aligned = !x.knew || (aligned(x.knew, 16) && aligned(x.vnew, 16));
-    if (decode_kernel_for(d, dtype) == GQA_KERNEL_DECODE_SPLIT && fast_aligned(q, k, v, out) &&
-        cand_aligned) {
+    if (decode_kernel_for(d, dtype) == GQA_KERNEL_DECODE_SPLIT) {
+        const bool cand_aligned = !x.knew || (aligned(x.knew, 16) && aligned(x.vnew, 16));
+        if (!fast_aligned(q, k, v, out) || !cand_aligned)
+            return GQA_ERR_ALIGN;
         const gqa::DecodePlan plan = gqa::plan_decode(B, C, Hq, Hkv, d, window);
         if (B > kMaxGridYZ || (int64_t)Hkv * plan.nhc > kMaxGridYZ)
             return GQA_ERR_SHAPE;
-        if (!workspace)
-            return GQA_ERR_NULL;
-        if (!aligned(workspace, 256))
-            return GQA_ERR_ALIGN;
-        if (workspace_bytes < plan.bytes)
-            return GQA_ERR_WORKSPACE;
+        // the workspace holds split partials only: without a split it is
+        // never touched and may be NULL
+        if (plan.nsplit > 1) {
+            if (!workspace)
+                return GQA_ERR_NULL;
+            if (!aligned(workspace, 256))
+                return GQA_ERR_ALIGN;
+            if (workspace_bytes < plan.bytes)
+                return GQA_ERR_WORKSPACE;
+        } else {
+            workspace = nullptr;
+        }
         return status_of(gqa::launch_decode_split(p, plan, workspace, s));
     }
     if (B > kMaxGridYZ || (int64_t)Hkv * ((r + 7) / 8) > kMaxGridYZ)
@@ -243,7 +256,8 @@ size_t gqa_decode_workspace_bytes(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
         return 0;
     if (B == 0 || decode_kernel_for(d, dtype) != GQA_KERNEL_DECODE_SPLIT)
         return 0;
-    return gqa::plan_decode(B, C, Hq, Hkv, d, window).bytes;
+    const gqa::DecodePlan plan = gqa::plan_decode(B, C, Hq, Hkv, d, window);
+    return plan.nsplit > 1 ? plan.bytes : 0;
 }
 
 int gqa_decode(const void *q, const void *k_cache, const void *v_cache, void *out,

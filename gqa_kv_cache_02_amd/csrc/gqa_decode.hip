@@ -622,6 +622,7 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window) {
 
 template <int D, bool kRecord, bool kExt>
 static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, hipStream_t s) {
+    // no workspace without a split (every row finishes in the split kernel)
     unsigned char *w = static_cast<unsigned char *>(ws);
     DecodeArgs a;
     a.q = static_cast<const uint16_t *>(p.q);
@@ -630,9 +631,9 @@ static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, h
     a.seqlens = p.seqlens;
     a.out = static_cast<uint16_t *>(p.out);
     a.records = p.records;
-    a.o_part = reinterpret_cast<float *>(w + plan.o_off);
-    a.lse_part = reinterpret_cast<float *>(w + plan.lse_off);
-    a.rec_part = reinterpret_cast<int32_t *>(w + plan.rec_off);
+    a.o_part = w ? reinterpret_cast<float *>(w + plan.o_off) : nullptr;
+    a.lse_part = w ? reinterpret_cast<float *>(w + plan.lse_off) : nullptr;
+    a.rec_part = w ? reinterpret_cast<int32_t *>(w + plan.rec_off) : nullptr;
     a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
     a.r = p.Hq / p.Hkv; a.nhc = plan.nhc; a.nsplit = plan.nsplit; a.chunk = plan.chunk;
     a.scale_log2 = p.scale * kLog2e;

@@ -30,6 +30,11 @@
  *     dot product.  It must be finite.
  *   - stream is a hipStream_t passed as void* (NULL = the default stream).
  *     Calls only enqueue work on it and return; they never synchronise.
+ *   - Alignment: every array to its element size; the workspace to 256
+ *     bytes.  bf16 calls with d = 64 or 128 run the matrix-core kernels,
+ *     which need q, k_cache, v_cache, out (and k_new, v_new) 16-byte
+ *     aligned; such a call with any of them misaligned is refused with
+ *     GQA_ERR_ALIGN (it is never rerouted to another kernel).
  *   - Every argument check happens on the host before anything is enqueued;
  *     on any error nothing is launched and out is left untouched (a failed
  *     call never half-advances anything, as the pages require of the cache).
@@ -58,7 +63,8 @@ typedef enum {
     GQA_ERR_SHAPE = 6,       /* negative B/T/C, T > C, or a grid limit exceeded    */
     GQA_ERR_OVERFLOW = 7,    /* an element count or byte size overflows int64      */
     GQA_ERR_WORKSPACE = 8,   /* workspace smaller than gqa_decode_workspace_bytes  */
-    GQA_ERR_ALIGN = 9,       /* a pointer is not aligned to its element size       */
+    GQA_ERR_ALIGN = 9,       /* a pointer is misaligned: to its element size, or to
+                                16 bytes for a matrix-core shape (bf16, d 64/128)  */
     GQA_ERR_HIP = 10,        /* the HIP runtime reported an error at launch        */
     GQA_ERR_SCALE = 11       /* scale is NaN or infinite                           */
 } gqa_status;
@@ -233,7 +239,9 @@ int gqa_decode_cache(const void *q, void *k_cache, void *v_cache, const void *k_
                      int32_t *records, void *stream);
 
 /* The kernel family gqa_prefill / gqa_decode would launch for these arguments
- * (GQA_KERNEL_NONE for a no-op or a refused call).  Alignment is assumed. */
+ * (GQA_KERNEL_NONE for a no-op or a refused call).  It depends on the
+ * arguments only: a call whose pointers do not meet that kernel's alignment
+ * is refused with GQA_ERR_ALIGN, so no other kernel ever runs in its place. */
 int gqa_prefill_kernel(int32_t B, int32_t T, int32_t C, int32_t Hq, int32_t Hkv, int32_t d,
                        int32_t window, int32_t dtype);
 int gqa_decode_kernel(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t d, int32_t window,

@@ -71,7 +71,7 @@ int refusals() {
     // Stand-in device pointers: every call below is refused by a host-side
     // check before anything could dereference them.
     void *P = reinterpret_cast<void *>(uintptr_t{4096});
-    const int32_t B = 2, C = 64, Hq = 8, Hkv = 2, d = 128;
+    const int32_t B = 2, C = 8000, Hq = 8, Hkv = 2, d = 128; // long enough to be split
     EXPECT(gqa_decode(P, P, P, P, nullptr, B, C, Hq, Hkv, d, 0, 0.5f, GQA_BF16, P, 1 << 20,
                       nullptr) == GQA_ERR_ZERO_WINDOW,
            "window 0 is not refused");
@@ -89,6 +89,16 @@ int refusals() {
     EXPECT(gqa_decode(P, P, P, P, nullptr, B, C, Hq, Hkv, d, -1, 0.5f, 7, P, need, nullptr) ==
                GQA_ERR_DTYPE,
            "an unknown dtype is not refused");
+    // a matrix-core shape with a pointer aligned to 2 bytes but not to 16
+    void *P2 = reinterpret_cast<void *>(uintptr_t{4096 + 2});
+    EXPECT(gqa_decode(P2, P, P, P, nullptr, B, C, Hq, Hkv, d, -1, 0.5f, GQA_BF16, P, need,
+                      nullptr) == GQA_ERR_ALIGN,
+           "a misaligned matrix-core decode is not refused");
+    EXPECT(gqa_prefill(P, P, P2, P, nullptr, 1, 64, 64, Hq, Hkv, d, -1, 0.5f, GQA_BF16,
+                       nullptr) == GQA_ERR_ALIGN,
+           "a misaligned matrix-core prefill is not refused");
+    EXPECT(gqa_decode_workspace_bytes(B, 64, Hq, Hkv, d, -1, GQA_BF16) == 0,
+           "a short cache (no split) asks for a workspace");
     // head map 8/2 -> 0,0,0,0,1,1,1,1; invalid inputs give -1
     for (int h = 0; h < 8; ++h)
         EXPECT(gqa_kv_head_for_query(h, 8, 2) == h / 4, "head map 8/2");

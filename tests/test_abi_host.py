@@ -121,15 +121,36 @@ def test_refusals_decode():
     assert _decode(C=-1) == SHAPE
     assert _decode(v=None) == NULL
     assert _decode(seqlens=ctypes.c_void_p(4098)) == ALIGN
-    need = gqa.lib().gqa_decode_workspace_bytes(2, 64, 8, 2, 128, -1, 1)
+    # a cache long enough to be split over several workgroups needs a
+    # workspace; a short one has no split and needs none
+    need = gqa.lib().gqa_decode_workspace_bytes(2, 8000, 8, 2, 128, -1, 1)
     assert need > 0
-    assert _decode(wsb=need - 1) == WORKSPACE
-    assert _decode(ws=None) == NULL
-    assert _decode(ws=ctypes.c_void_p(4096 + 16)) == ALIGN
+    assert gqa.lib().gqa_decode_workspace_bytes(2, 64, 8, 2, 128, -1, 1) == 0
+    assert _decode(C=8000, wsb=need - 1) == WORKSPACE
+    assert _decode(C=8000, ws=None) == NULL
+    assert _decode(C=8000, ws=ctypes.c_void_p(4096 + 16)) == ALIGN
     assert _decode(B=70000) == SHAPE
     assert _decode(B=0, q=None, k=None, v=None, out=None) == OK
     assert gqa.lib().gqa_decode_records(P, P, P, P, None, 2, 64, 8, 2, 128, -1, 0.5, 1, P,
                                         1 << 30, None, None) == NULL
+
+
+def test_matrix_core_shapes_refuse_misaligned_pointers():
+    # bf16 with d = 64 or 128 runs the matrix-core kernels, which move 16
+    # bytes per lane: a pointer aligned to its element size but not to 16
+    # bytes is refused, never rerouted to another kernel
+    P2 = ctypes.c_void_p(4096 + 2)
+    for name in ("q", "k", "v", "out"):
+        assert _decode(**{name: P2}) == ALIGN, name
+        assert _decode(C=8000, **{name: P2}) == ALIGN, name
+        for d in (64, 128):
+            assert _prefill(dtype=1, d=d, **{name: P2}) == ALIGN, (name, d)
+            assert _prefix(dtype=1, d=d, **{name: P2}) == ALIGN, (name, d)
+    assert _dcache(kn=P2, vn=P) == ALIGN
+    assert _dcache(kn=P, vn=P2) == ALIGN
+    # the kernel a call runs depends on its arguments only
+    assert gqa.decode_kernel(2, 64, 8, 2, 128) == "decode_split"
+    assert gqa.prefill_kernel(1, 4, 4, 4, 2, 64) == "prefill_mfma"
 
 
 def test_workspace_size_and_kernel_choice():
@@ -200,12 +221,14 @@ def test_refusals_decode_cache():
     assert _dcache(kn=P) == NULL                 # the key without the value
     assert _dcache(vn=P) == NULL
     assert _dcache(kn=P_ODD, vn=P) == ALIGN
-    assert _dcache(ring=0, window=-1, wsb=0) == WORKSPACE
+    assert _dcache(ring=0, window=-1, C=8000, wsb=0) == WORKSPACE
     assert _dcache(B=0, q=None, k=None, v=None, out=None) == OK
     # a rolling cache sizes its workspace from the window, like gqa_decode
     L = gqa.lib()
-    need = L.gqa_decode_workspace_bytes(2, 64, 8, 2, 128, 16, 1)
-    assert _dcache(wsb=need - 1) == WORKSPACE
+    need = L.gqa_decode_workspace_bytes(2, 8000, 8, 2, 128, 4000, 1)
+    assert need > 0
+    assert _dcache(C=8000, window=4000, wsb=need - 1) == WORKSPACE
+    assert _dcache(C=8000, window=4000, ws=None) == NULL
 
 
 def _decode_plan_bytes(B, C, hq, hkv, d, window):
@@ -223,7 +246,9 @@ def _decode_plan_bytes(B, C, hq, hkv, d, window):
     nsplit = -(-elig // chunk) if elig > 0 else 0
     rows = B * hq * nsplit
     a256 = lambda x: (x + 255) // 256 * 256
-    return a256(rows * d * 4) + a256(rows * 4) + a256(rows * 16), nsplit, chunk
+    # without a split every row finishes in one workgroup: no workspace
+    need = a256(rows * d * 4) + a256(rows * 4) + a256(rows * 16) if nsplit > 1 else 0
+    return need, nsplit, chunk
 
 
 def test_decode_plan_even_chunks():

@@ -146,29 +146,53 @@ def test_prefill_mfma_sweep(d):
             assert np.array_equal(_np(rec).astype(np.int32), rrec), (hq, hkv, w)
 
 
+def _probe_values(T, hkv):
+    """V channels [1, g, j, j^2] of the zero-Q/K probe (the pages' own device
+    in "Follow four query heads into two shared groups": with Q = K = 0 every
+    permitted key gets the same weight, so the output is the mean of V over
+    the permitted set).  Returns V in float32 before the bf16 cast and the
+    stored (bf16-rounded) j^2 column in float64."""
+    v = torch.zeros((hkv, T, 4), dtype=torch.float32)
+    j = torch.arange(T, dtype=torch.float32)
+    for g in range(hkv):
+        v[g, :, 0] = 1.0
+        v[g, :, 1] = float(g)
+        v[g, :, 2] = j
+        v[g, :, 3] = j * j
+    j2 = v[0, :, 3].to(torch.bfloat16).double().numpy()
+    return v, j2
+
+
+def _mean_over(vals, lo, hi):
+    """Mean of vals[lo..hi] (inclusive) for arrays of bounds, in fp64."""
+    cs = np.concatenate([[0.0], np.cumsum(vals)])
+    return (cs[hi + 1] - cs[lo]) / (hi - lo + 1)
+
+
 def test_prefill_zero_qk_probe():
-    # equal weights: channel 2 of V holds the key index, so the output is the
-    # mean permitted key index (l + t) / 2 on every row of the MFMA kernel
+    # equal weights: V channels [1, g, j, j^2] give 1, the KV head, the mean
+    # permitted key index (l + t) / 2 and the mean stored j^2 on every row of
+    # the MFMA kernel; windows 1, 2, BN-1, BN, BN+1 (BN = 64) and 31
     B, T, hq, hkv, d = 2, 200, 8, 2, 128
     q = torch.zeros((B, hq, T, d), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros((B, hkv, T, d), dtype=torch.bfloat16, device=DEV)
     v = torch.zeros((B, hkv, T, d), dtype=torch.float32)
-    for g in range(hkv):
-        v[:, g, :, 0] = 1.0
-        v[:, g, :, 1] = float(g)
-        v[:, g, :, 2] = torch.arange(T, dtype=torch.float32)
+    chans, j2 = _probe_values(T, hkv)
+    v[:, :, :, :4] = chans[None]
     v = v.to(torch.bfloat16).to(DEV)
-    for w in (None, 1, 31, 64, 65):
+    for w in (None, 1, 2, 31, 63, 64, 65):
         out, _ = run_prefill(q, k, v, seqlens=[200, 77], window=w)
         o = _np(out)
         for b, n in enumerate((200, 77)):
             t = np.arange(T)
-            lo = np.zeros(T) if w is None else np.maximum(0, t - w + 1)
+            lo = np.zeros(T, np.int64) if w is None else np.maximum(0, t - w + 1)
             mean = (lo + t) / 2.0
+            mean2 = _mean_over(j2, lo, t)
             act = t < n
             assert (o[b, act, :, 0] == 1.0).all()
             assert (o[b, act, :, 1] == (np.arange(hq) // (hq // hkv))[None, :]).all()
             assert (np.abs(o[b, act, :, 2] - mean[act, None]) <= np.abs(mean[act, None]) * 2 ** -8).all()
+            assert (np.abs(o[b, act, :, 3] - mean2[act, None]) <= mean2[act, None] * 2 ** -8).all(), w
             assert not o[b, ~act].any()
 
 
@@ -244,30 +268,29 @@ def test_decode_equals_prefill_row():
 
 def test_zero_qk_probe_index_sets():
     # Q = K = 0 gives equal weights; with V channels [1, g, j, j^2] the outputs
-    # are 1, the KV head, the mean key index and the mean of j^2 over the
-    # permitted set -- exact in fp32 arithmetic and bf16 storage for j <= 256.
+    # are 1, the KV head, the mean key index and the mean of the stored j^2
+    # over the permitted set (exact up to the bf16 rounding of the output)
     for d in (64, 128):
         B, hq, hkv, C = 3, 8, 2, 256
         q = torch.zeros((B, hq, d), dtype=torch.bfloat16, device=DEV)
         k = torch.zeros((B, hkv, C, d), dtype=torch.bfloat16, device=DEV)
         v = torch.zeros((B, hkv, C, d), dtype=torch.float32)
-        j = torch.arange(C, dtype=torch.float32)
-        for g in range(hkv):
-            v[:, g, :, 0] = 1.0
-            v[:, g, :, 1] = float(g)
-            v[:, g, :, 2] = j
+        chans, j2 = _probe_values(C, hkv)
+        v[:, :, :, :4] = chans[None]
         v = v.to(torch.bfloat16).to(DEV)
         seqlens = [256, 100, 17]
-        for w in (None, 1, 31, 32, 33, 64):
+        for w in (None, 1, 2, 31, 32, 33, 64):
             out, _ = run_decode(q, k, v, seqlens=seqlens, window=w)
             o = _np(out)
             for b, n in enumerate(seqlens):
                 lo = 0 if w is None else max(0, n - w)
+                mean = (lo + n - 1) / 2.0
+                mean2 = float(_mean_over(j2, np.array([lo]), np.array([n - 1]))[0])
                 for h in range(hq):
                     assert o[b, h, 0] == 1.0
                     assert o[b, h, 1] == float(h // (hq // hkv))
-                    mean = (lo + n - 1) / 2.0
                     assert abs(o[b, h, 2] - mean) <= abs(mean) * 2 ** -8, (w, b, h)
+                    assert abs(o[b, h, 3] - mean2) <= mean2 * 2 ** -8, (w, b, h)
 
 
 def test_dirty_workspace_and_side_stream():
@@ -341,6 +364,43 @@ def test_refused_call_leaves_output_untouched():
     assert (out == 3.0).all() and (outx == 5.0).all()
 
 
+def test_no_split_decode_takes_a_null_workspace():
+    # a cache short enough for one workgroup per row needs no workspace
+    # (its size is 0) and the library accepts NULL for it
+    B, C, hq, hkv, d = 3, 100, 8, 2, 128
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 31, DEV)
+    assert gqa.decode_workspace_bytes(B, C, hq, hkv, d) == 0
+    sl = torch.tensor([100, 37, 0], dtype=torch.int32, device=DEV)
+    out = torch.full((B, hq, d), 9.0, dtype=torch.bfloat16, device=DEV)
+    rc = gqa.lib().gqa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              sl.data_ptr(), B, C, hq, hkv, d, -1, 1.0 / math.sqrt(d), 1,
+                              None, 0, None)
+    torch.cuda.synchronize()
+    assert rc == 0
+    ref, _, _ = oracle.decode(_np(q), _np(k), _np(v), seqlens=[100, 37, 0])
+    assert _maxerr(_np(out), ref) <= BF16_TOL
+
+
+def test_misaligned_matrix_core_call_is_refused():
+    # q 2 bytes past a 16-byte boundary: refused (GQA_ERR_ALIGN), out untouched
+    B, C, hq, hkv, d = 2, 300, 8, 2, 64
+    _, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 32, DEV)
+    buf = torch.zeros(B * hq * d + 1, dtype=torch.bfloat16, device=DEV)
+    q = buf[1:].view(B, hq, d)
+    assert q.data_ptr() % 16 == 2
+    out = torch.full((B, hq, d), 4.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gqa.GQAError) as e:
+        gqa.decode(q, k, v, out=out)
+    assert e.value.status == 9
+    qp = torch.zeros(B * hq * 16 * d + 1, dtype=torch.bfloat16, device=DEV)[1:].view(B, hq, 16, d)
+    outp = torch.full((B, 16, hq, d), 4.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gqa.GQAError) as e:
+        gqa.prefill(qp, k, v, out=outp)
+    assert e.value.status == 9
+    torch.cuda.synchronize()
+    assert (out == 4.0).all() and (outp == 4.0).all()
+
+
 def test_empty_inputs():
     q = torch.zeros((0, 8, 128), dtype=torch.bfloat16, device=DEV)
     k = torch.zeros((0, 2, 16, 128), dtype=torch.bfloat16, device=DEV)
@@ -356,7 +416,7 @@ def test_empty_inputs():
 
 
 # ---------------------------------------------------------------------------
-# full-size configurations: sampled rows against the oracle, properties for all
+# full-size configurations: every element and every record against the oracle
 # ---------------------------------------------------------------------------
 
 def _convex_bounds_ok(out, v, hq, hkv, lo, hi):
@@ -373,20 +433,17 @@ def _convex_bounds_ok(out, v, hq, hkv, lo, hi):
     return True
 
 
-def _decode_full_check(B, C, hq, hkv, d, seqlens, window, seed, sample_b):
+def _decode_full_check(B, C, hq, hkv, d, seqlens, window, seed):
     q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, seed, DEV)
     out, rec = run_decode(q, k, v, seqlens=seqlens, window=window, records=True)
     assert bool(torch.isfinite(out.float()).all())
-    # index sets of every row, from the oracle on zero inputs of width 1
-    _, _, rrec = oracle.decode(np.zeros((B, hq, 1)), np.zeros((B, hkv, C, 1)),
-                               np.zeros((B, hkv, C, 1)), seqlens=seqlens, window=window,
-                               want_records=True)
+    # every output element and every row's index set against the oracle on
+    # the same bits (the pages' own comparison checks every logit)
+    ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=seqlens, window=window,
+                                 want_records=True)
+    err = _maxerr(_np(out), ref)
+    assert err <= BF16_TOL, err
     assert np.array_equal(_np(rec).astype(np.int32), rrec)
-    # values of sampled batch rows, one by one
-    for b in sample_b:
-        ref, _, _ = oracle.decode(_np(q[b:b + 1]), _np(k[b:b + 1]), _np(v[b:b + 1]),
-                                  seqlens=[seqlens[b]], window=window)
-        assert _maxerr(_np(out[b:b + 1]), ref) <= BF16_TOL, b
     lo = [0 if window is None else max(0, n - window) for n in seqlens]
     hi = [n - 1 for n in seqlens]
     assert _convex_bounds_ok(out, v, hq, hkv, lo, hi)
@@ -404,14 +461,14 @@ def _decode_full_check(B, C, hq, hkv, d, seqlens, window, seed, sample_b):
 def test_full_decode_b8_hq32_hkv8_d128_n8000():
     cfg = synth.CONFIGS["decode_b8_hq32_hkv8_d128_n8000"]
     _decode_full_check(cfg["B"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"], [cfg["n"]] * cfg["B"],
-                       cfg["window"], cfg["seed"], sample_b=(0, 5, 7))
+                       cfg["window"], cfg["seed"])
 
 
 @pytest.mark.parametrize("hkv", [8, 2, 1])
 def test_full_decode_endpoint_sweep(hkv):
     cfg = synth.CONFIGS["decode_sweep_b16_hq8_d128_n8000"]
     _decode_full_check(cfg["B"], cfg["C"], cfg["Hq"], hkv, cfg["d"], [cfg["n"]] * cfg["B"],
-                       cfg["window"], cfg["seed"] + hkv, sample_b=(0, 15))
+                       cfg["window"], cfg["seed"] + hkv)
 
 
 def test_full_decode_endpoints_equal_explicit_repeat():
@@ -438,10 +495,10 @@ def test_full_decode_ragged_window():
     lo, hi = cfg["n"]
     seqlens = synth.ragged_lengths(cfg["B"], lo, hi, cfg["seed"]).tolist()
     _decode_full_check(cfg["B"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"], seqlens,
-                       cfg["window"], cfg["seed"], sample_b=(0, 1, 17, 31))
+                       cfg["window"], cfg["seed"])
 
 
-def test_full_prefill_t4096_sampled_rows():
+def test_full_prefill_t4096():
     cfg = synth.CONFIGS["prefill_b1_t4096_hq32_hkv8_d128"]
     B, T, hq, hkv, d = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
     q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, cfg["seed"], DEV)
@@ -453,16 +510,18 @@ def test_full_prefill_t4096_sampled_rows():
     gqa.prefill(q, k, v, out=plain)
     torch.cuda.synchronize()
     assert torch.equal(plain, out)
-    r = _np(rec).astype(np.int64)
+    # every output element and every row's record (KV head, lowest and
+    # highest key, count, XOR of the keys) against the oracle
+    ref, _, rrec = oracle.prefill(_np(q), _np(k), _np(v), want_records=True)
+    err = _maxerr(o, ref)
+    assert err <= BF16_TOL, err
+    r = _np(rec).astype(np.int32)
+    assert np.array_equal(r, rrec)
+    # and the closed form of the causal index sets: keys 0..t, XOR 0^1^..^t
     t = np.arange(T)[None, :, None]
-    h = np.arange(hq)[None, None, :]
-    assert (r[..., 0] == h // (hq // hkv)).all()
+    xor_to = np.where(t % 4 == 0, t, np.where(t % 4 == 1, 1, np.where(t % 4 == 2, t + 1, 0)))
     assert (r[..., 1] == 0).all() and (r[..., 2] == t).all() and (r[..., 3] == t + 1).all()
-    # sampled rows: the oracle's decode at n = t + 1 is prefill row t
-    kn, vn = _np(k), _np(v)
-    for tt in (0, 1, 63, 64, 127, 128, 1000, 2047, 2048, 4094, 4095):
-        ref, _, _ = oracle.decode(_np(q[:, :, tt]), kn, vn, seqlens=[tt + 1])
-        assert _maxerr(o[:, tt], ref) <= BF16_TOL, tt
+    assert (r[..., 4] == xor_to).all()
 
 
 def test_offsets_beyond_2_31_elements():
