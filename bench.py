@@ -48,7 +48,21 @@ Prints ONE JSON line.
   measures the host.
   cpu_baseline   the fp64 oracle (plain C, OpenMP) on the host cores, on the
                  same decode workload; with the CPU model, the process's
-                 affinity set and a one-thread figure on one batch row.
+                 affinity set and a one-thread figure on one batch row.  Every
+                 other leg carries its own `cpu_baseline`: the oracle on that
+                 leg's whole workload (same inputs, same unit), with the core
+                 count.
+  traffic        each leg's HBM bytes per call measured by rocprofv3 counters
+                 (profiles/bench_workloads_traffic.txt, one process per leg so
+                 that no dispatch is attributed to the wrong leg), while the
+                 kernel source still has the hash they were taken with.
+
+    python bench.py --leg NAME [--steps K] [--copy-calibration]
+runs one leg only (decode, prefill, prefix, ring, sweep8, sweep2, sweep1,
+ragged), for hardware-counter runs; and
+    python bench.py --summarize-counters DIR
+turns the counter CSVs of those runs (DIR/<leg>/{fetch,write}/...) into the
+traffic summary committed under profiles/.
 """
 from __future__ import annotations
 
@@ -67,7 +81,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 COPY_CAL_BYTES = 1 << 30  # plain copy used to calibrate the traffic counters
 DECODE_SRC = os.path.join(ROOT, "gqa_kv_cache_02_amd", "csrc", "gqa_decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_b8_hq32_hkv8_d128_n8000_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bench_workloads_traffic.txt")
 PREFILL_SRC = os.path.join(ROOT, "gqa_kv_cache_02_amd", "csrc", "gqa_prefill.hip")
 MFMA_FILE = os.path.join(ROOT, "profiles", "prefill_b1_t4096_hq32_hkv8_d128_mfma_counters.txt")
 
@@ -110,22 +124,172 @@ def measured_mfma():
         return None
 
 
-def measured_traffic():
-    """HBM bytes per decode call from the committed counter summary, or None
-    when it is missing or was taken on a different kernel source."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
+# Legs of the benchmark: the kernel source each one runs, and the library
+# kernels of one call (the first is launched once per call).
+LEG_SOURCE = {"decode": DECODE_SRC, "ring": DECODE_SRC, "sweep8": DECODE_SRC,
+              "sweep2": DECODE_SRC, "sweep1": DECODE_SRC, "ragged": DECODE_SRC,
+              "prefill": PREFILL_SRC, "prefix": PREFILL_SRC}
+LEG_KERNELS = {leg: ("decode_kernel", "decode_merge_kernel") for leg in LEG_SOURCE}
+LEG_KERNELS["prefill"] = LEG_KERNELS["prefix"] = ("prefill_mfma_kernel", "prefix_merge_kernel")
+
+
+def _summary_values(path):
     vals = {}
-    for ln in open(TRAFFIC_FILE):
+    for ln in open(path):
         if "=" in ln and not ln.lstrip().startswith("#"):
             k, v = ln.split("=", 1)
             vals[k.strip()] = v.strip()
-    if vals.get("decode_source_sha256_16") != source_hash(DECODE_SRC):
+    return vals
+
+
+def _source_key(src):
+    return "prefill_source_sha256_16" if src == PREFILL_SRC else "decode_source_sha256_16"
+
+
+def measured_traffic(leg="decode"):
+    """HBM bytes per call of a leg from the committed counter summary, or None
+    when it is missing or was taken on a different kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = _summary_values(TRAFFIC_FILE)
+    src = LEG_SOURCE[leg]
+    if vals.get(_source_key(src)) != source_hash(src):
         return None
     try:
-        return int(float(vals["hbm_bytes_per_call"]))
+        return int(float(vals[f"{leg}.hbm_bytes_per_call"]))
     except (KeyError, ValueError):
         return None
+
+
+def _counter_rows(dirpath):
+    """(dispatch id, kernel name, value in KiB) of every row of the rocprofv3
+    counter-collection CSVs under dirpath (one counter per run)."""
+    import csv
+    import glob
+
+    rows = []
+    for f in sorted(glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"),
+                              recursive=True)):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], float(r["Counter_Value"])))
+    # a counter read over several instances is one row each: sum per dispatch
+    per = {}
+    for did, name, val in rows:
+        n, v = per.get(did, (name, 0.0))
+        per[did] = (n, v + val)
+    return [(did, n, v) for did, (n, v) in sorted(per.items())]
+
+
+def _leg_counter_bytes(rows, leg):
+    """Copy-calibration KiB, and (calls, summed KiB over the leg's kernels)."""
+    copies = [v for _, n, v in rows if "copy" in n.lower()]
+    cal = max(copies) if copies else None
+    main, merge = LEG_KERNELS[leg]
+    calls = sum(1 for _, n, _ in rows if main in n and "merge" not in n)
+    kib = sum(v for _, n, v in rows if (main in n and "merge" not in n) or merge in n)
+    return cal, calls, kib
+
+
+def algorithmic_bytes(leg):
+    """The bytes each leg's workload must move, as the bench legs count them
+    (None for the prefill legs, whose roofline is matrix-core work)."""
+    from gqa_kv_cache_02_amd import synth
+
+    if leg == "decode":
+        c = synth.CONFIGS["decode_b8_hq32_hkv8_d128_n8000"]
+        return decode_bytes(c["B"], c["Hq"], c["Hkv"], c["d"], c["n"])
+    if leg.startswith("sweep"):
+        c = synth.CONFIGS["decode_sweep_b16_hq8_d128_n8000"]
+        return decode_bytes(c["B"], c["Hq"], int(leg[5:]), c["d"], c["n"])
+    if leg in ("ragged", "ring"):
+        name = "decode_ragged_b32_hq8_hkv2_d64_w4096" if leg == "ragged" \
+            else "ring_b32_hq8_hkv2_d64_w4096"
+        c = synth.CONFIGS[name]
+        lens = synth.ragged_lengths(c["B"], c["n"][0], c["n"][1], c["seed"]).tolist()
+        cells = sum(min(int(n), c["window"]) for n in lens)
+        nbytes = 2 * c["Hkv"] * cells * c["d"] * 2 + 2 * c["B"] * c["Hq"] * c["d"] * 2
+        if leg == "ring":  # the candidate read and committed
+            nbytes += 4 * c["B"] * c["Hkv"] * c["d"] * 2
+        return nbytes
+    return None
+
+
+def summarize_counters(dirpath):
+    """Text of the per-leg traffic summary from counter runs laid out as
+    dirpath/<leg>/fetch/... (FETCH_SIZE) and dirpath/<leg>/write/...
+    (WRITE_SIZE), each made by `bench.py --leg <leg> --copy-calibration`."""
+    cmd_f = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT/<leg>/fetch -o ctr -- "
+             "python3 bench.py --leg <leg> --steps 5 --warmup 1 --copy-calibration")
+    lines = [
+        "# HBM traffic per call of each bench.py leg, from the rocprofv3 counters",
+        "# FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each leg and each counter in a",
+        "# process of its own, so that every dispatch of the library's kernels in a run",
+        "# belongs to that leg.  Each run also makes a plain 1 GiB device copy; the",
+        "# counters are scaled by what they read for it (factor = 1 GiB / counter).",
+        "#",
+        "# Commands (from the repository root; TMPDIR=/tmp), for every leg in",
+        "# decode prefill prefix ring sweep8 sweep2 sweep1 ragged:",
+        f"#   {cmd_f}",
+        "#   (the same with --pmc WRITE_SIZE and -d OUT/<leg>/write)",
+        "#   python3 bench.py --summarize-counters OUT",
+        "#",
+        "# leg       calls  fetch_scale write_scale   read MB  written MB   HBM MB/call  "
+        "algorithmic MB  ratio",
+    ]
+    vals = []
+    for leg in LEG_SOURCE:
+        fr = _counter_rows(os.path.join(dirpath, leg, "fetch"))
+        wr = _counter_rows(os.path.join(dirpath, leg, "write"))
+        if not fr or not wr:
+            continue
+        fcal, fcalls, fkib = _leg_counter_bytes(fr, leg)
+        wcal, wcalls, wkib = _leg_counter_bytes(wr, leg)
+        if not fcal or not wcal or fcalls == 0 or fcalls != wcalls:
+            continue
+        fs = COPY_CAL_BYTES / (fcal * 1024.0)
+        ws = COPY_CAL_BYTES / (wcal * 1024.0)
+        rd = fkib * 1024.0 * fs / fcalls
+        wt = wkib * 1024.0 * ws / wcalls
+        alg = algorithmic_bytes(leg)
+        ratio = f"{(rd + wt) / alg:6.3f}" if alg else "   -  "
+        alg_s = f"{alg / 1e6:14.2f}" if alg else "             -"
+        lines.append(f"# {leg:8s} {fcalls:6d} {fs:11.4f} {ws:11.4f} {rd / 1e6:9.2f} "
+                     f"{wt / 1e6:11.3f} {(rd + wt) / 1e6:13.2f} {alg_s} {ratio}")
+        vals.append(f"{leg}.hbm_bytes_per_call = {int(round(rd + wt))}")
+    lines.append("#")
+    lines.append("# The prefill legs read Q and K/V and write O (and, for the split prefix")
+    lines.append("# rows, partials that the merge reads back); their roofline is matrix-core work.")
+    lines += vals
+    lines.append(f"decode_source_sha256_16 = {source_hash(DECODE_SRC)}")
+    lines.append(f"prefill_source_sha256_16 = {source_hash(PREFILL_SRC)}")
+    return "\n".join(lines) + "\n"
+
+
+def _f64(t):
+    """A device tensor's stored values, widened exactly to float64 on the host."""
+    import numpy as np
+
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def _oracle_baseline(run, work, unit_scale, unit, sample, budget_s=2.0, max_runs=50):
+    """The oracle as it stands (`run` calls it on a leg's whole workload, on
+    inputs already widened to float64), timed on the host cores: at least one
+    run, then more until about budget_s; work / time in the leg's unit."""
+    import oracle
+
+    runs, total = 0, 0.0
+    while runs == 0 or (total < budget_s and runs < max_runs):
+        t0 = time.perf_counter()
+        run()
+        total += time.perf_counter() - t0
+        runs += 1
+    per = total / runs
+    return dict(value=round(work / per / unit_scale, 5), unit=unit, cores=oracle.threads(),
+                kind="oracle", seconds_per_call=round(per, 4),
+                sample=f"{sample}; {runs} run(s) of {per:.4f} s; inputs widened to float64 "
+                       "before timing")
 
 
 def bench_decode(torch, gqa, synth, steps, warmup):
@@ -178,7 +342,7 @@ def bench_decode(torch, gqa, synth, steps, warmup):
                 nbytes=decode_bytes(B, hq, hkv, d, n), q=q, k=k0, v=v0, seqlens=[n] * B)
 
 
-def bench_prefill(torch, gqa, synth, steps, warmup):
+def bench_prefill(torch, gqa, synth, steps, warmup, cpu=False):
     cfg = synth.CONFIGS["prefill_b1_t4096_hq32_hkv8_d128"]
     B, T, hq, hkv, d = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
     dev = torch.device("cuda:0")
@@ -208,16 +372,25 @@ def bench_prefill(torch, gqa, synth, steps, warmup):
     flops = prefill_flops(hq, d, T, B)
     tflops = flops / (ms * 1e-3) / 1e12
     tflops_call = flops / (ms_call * 1e-3) / 1e12
-    return dict(workload="gqa_prefill_b1_t4096_hq32_hkv8_d128_causal_bf16",
-                kernel=gqa.prefill_kernel(B, T, T, hq, hkv, d), ms=round(ms, 5),
-                flops=flops, tflops=round(tflops, 2),
-                frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
-                tokens_per_s=round(B * T / (ms * 1e-3), 1),
-                timing="back-to-back calls between two HIP events on the launch stream",
-                per_call={"ms": round(ms_call, 5), "tflops": round(tflops_call, 2),
-                          "frac_of_bf16_peak": round(tflops_call / BF16_PEAK_TFLOPS, 4),
-                          "timing": "HIP events on the launch stream around each call"},
-                mfma_counters=measured_mfma())
+    res = dict(workload="gqa_prefill_b1_t4096_hq32_hkv8_d128_causal_bf16",
+               kernel=gqa.prefill_kernel(B, T, T, hq, hkv, d), ms=round(ms, 5),
+               flops=flops, tflops=round(tflops, 2),
+               frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
+               tokens_per_s=round(B * T / (ms * 1e-3), 1),
+               timing="back-to-back calls between two HIP events on the launch stream",
+               per_call={"ms": round(ms_call, 5), "tflops": round(tflops_call, 2),
+                         "frac_of_bf16_peak": round(tflops_call / BF16_PEAK_TFLOPS, 4),
+                         "timing": "HIP events on the launch stream around each call"},
+               mfma_counters=measured_mfma(), traffic=measured_traffic("prefill"))
+    if cpu:
+        import oracle
+
+        qn, kn, vn = _f64(q), _f64(k), _f64(v)
+        res["cpu_baseline"] = _oracle_baseline(
+            lambda: oracle.prefill(qn, kn, vn), flops, 1e12, "TFLOP/s",
+            "the whole causal prefill workload (B=1, T=4096, Hq=32, Hkv=8, d=128) in fp64",
+            budget_s=0.0)
+    return res
 
 
 B2B = "back-to-back calls between two HIP events on the launch stream"
@@ -256,7 +429,7 @@ def prefix_flops(Hq, d, C, Tq, B=1):
     return 4 * Hq * d * B * pairs
 
 
-def bench_prefix(torch, gqa, synth, steps, warmup):
+def bench_prefix(torch, gqa, synth, steps, warmup, cpu=False):
     cfg = synth.CONFIGS["chunk_b1_tq512_c4096_hq32_hkv8_d128"]
     B, Tq, C, hq, hkv, d = cfg["B"], cfg["Tq"], cfg["C"], cfg["Hq"], cfg["Hkv"], cfg["d"]
     dev = torch.device("cuda:0")
@@ -268,14 +441,22 @@ def bench_prefix(torch, gqa, synth, steps, warmup):
                                                                   workspace=ws), steps, warmup)
     flops = prefix_flops(hq, d, C, Tq, B)
     tflops = flops / (ms * 1e-3) / 1e12
-    return dict(workload="gqa_prefill_prefix_b1_tq512_c4096_hq32_hkv8_d128_bf16",
-                ms=round(ms, 5), flops=flops, tflops=round(tflops, 2),
-                frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
-                tokens_per_s=round(B * Tq / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5),
-                timing=f"{B2B}; {PER_CALL}")
+    res = dict(workload="gqa_prefill_prefix_b1_tq512_c4096_hq32_hkv8_d128_bf16",
+               ms=round(ms, 5), flops=flops, tflops=round(tflops, 2),
+               frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
+               tokens_per_s=round(B * Tq / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5),
+               timing=f"{B2B}; {PER_CALL}", traffic=measured_traffic("prefix"))
+    if cpu:
+        import oracle
+
+        qn, kn, vn = _f64(q), _f64(k), _f64(v)
+        res["cpu_baseline"] = _oracle_baseline(
+            lambda: oracle.attend_prefix(qn, kn, vn), flops, 1e12, "TFLOP/s",
+            "the whole prefix workload (512 new rows against 4096 cells) in fp64")
+    return res
 
 
-def bench_ring(torch, gqa, synth, steps, warmup):
+def bench_ring(torch, gqa, synth, steps, warmup, cpu=False):
     cfg = synth.CONFIGS["ring_b32_hq8_hkv2_d64_w4096"]
     B, hq, hkv, d, w = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["window"]
     lo, hi = cfg["n"]
@@ -296,6 +477,9 @@ def bench_ring(torch, gqa, synth, steps, warmup):
     out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=dev)
     ws = torch.empty(max(1, gqa.decode_workspace_bytes(B, w, hq, hkv, d, w)), dtype=torch.uint8,
                      device=dev)
+    # the calls commit their candidate into the cache: keep the cache as it
+    # was for the oracle
+    k_orig, v_orig = (k0.clone(), v0.clone()) if cpu else (None, None)
     ms, ms_call = _time_calls(torch, lambda i: gqa.decode_cache(q, ks[i % copies], vs[i % copies],
                                                        k_new=kn, v_new=vn, seqlens=seqlens,
                                                        window=w, ring=True, out=out,
@@ -303,14 +487,25 @@ def bench_ring(torch, gqa, synth, steps, warmup):
     cells = int(sum(min(int(n), w) for n in lens.tolist()))
     nbytes = 2 * hkv * cells * d * 2 + 2 * B * hq * d * 2 + 4 * B * hkv * d * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return dict(workload="gqa_decode_cache_ring_b32_hq8_hkv2_d64_w4096_bf16",
-                ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
-                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
-                tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
-                per_call_ms=round(ms_call, 5), timing=f"{B2B}; {PER_CALL}")
+    res = dict(workload="gqa_decode_cache_ring_b32_hq8_hkv2_d64_w4096_bf16",
+               ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
+               frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+               tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
+               per_call_ms=round(ms_call, 5), timing=f"{B2B}; {PER_CALL}",
+               traffic=measured_traffic("ring"))
+    if cpu:
+        import oracle
+
+        qn, kn0, vn0, knn, vnn = _f64(q), _f64(k_orig), _f64(v_orig), _f64(kn), _f64(vn)
+        sl = lens.tolist()
+        res["cpu_baseline"] = _oracle_baseline(
+            lambda: oracle.decode_cache(qn, kn0, vn0, knn, vnn, seqlens=sl, window=w, ring=True),
+            nbytes, 1e9, "GB/s", "the whole rolling-cache workload (B=32, Hq=8, Hkv=2, d=64, "
+            "w=C=4096, ragged lengths, committed candidate) in fp64")
+    return res
 
 
-def bench_sweep(torch, gqa, synth, steps, warmup):
+def bench_sweep(torch, gqa, synth, steps, warmup, cpu=False, hkvs=None):
     """Endpoint sweep: B=16, Hq=8, d=128, 8000 cached cells; MHA, GQA group 4
     and MQA.  A K/V copy holds 524, 131 or 66 MB; 4 copies rotate for Hkv >= 2
     and 6 for Hkv = 1, so no step finds its cache in the 256 MB Infinity Cache
@@ -319,7 +514,7 @@ def bench_sweep(torch, gqa, synth, steps, warmup):
     B, hq, d, n = cfg["B"], cfg["Hq"], cfg["d"], cfg["n"]
     dev = torch.device("cuda:0")
     res = []
-    for hkv in cfg["Hkv"]:
+    for hkv in (cfg["Hkv"] if hkvs is None else hkvs):
         copies = 4 if hkv >= 2 else 6
         q, k0, v0 = synth.decode_inputs(B, n, hq, hkv, d, torch.bfloat16, cfg["seed"], dev)
         ks, vs = [k0], [v0]
@@ -334,15 +529,26 @@ def bench_sweep(torch, gqa, synth, steps, warmup):
                                                      workspace=ws), steps, warmup)
         nbytes = decode_bytes(B, hq, hkv, d, n)
         gbs = nbytes / (ms * 1e-3) / 1e9
-        res.append(dict(Hkv=hkv, ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
-                        frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
-                        tokens_per_s=round(B / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5)))
+        leg = dict(Hkv=hkv, ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
+                   frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+                   tokens_per_s=round(B / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5),
+                   traffic=measured_traffic(f"sweep{hkv}"))
+        if cpu:
+            import oracle
+
+            qn, kn, vn = _f64(q), _f64(k0), _f64(v0)
+            leg["cpu_baseline"] = _oracle_baseline(
+                lambda: oracle.decode(qn, kn, vn), nbytes, 1e9, "GB/s",
+                f"the whole sweep workload at Hkv={hkv} (B=16, Hq=8, d=128, 8000 cells) in fp64",
+                budget_s=1.0)
+            del qn, kn, vn
+        res.append(leg)
         del ks, vs, q, k0, v0
     return dict(workload="gqa_decode_sweep_b16_hq8_d128_n8000_bf16", results=res,
                 timing=f"{B2B}; {PER_CALL}")
 
 
-def bench_ragged_window(torch, gqa, synth, steps, warmup):
+def bench_ragged_window(torch, gqa, synth, steps, warmup, cpu=False):
     """Ragged sliding-window decode over a linear cache: B=32, Hq=8, Hkv=2,
     d=64, lengths uniform in [1, 32768], window 4096.  GB/s of the K/V cells
     inside each row's window, read once per KV group; 6 rotated copies."""
@@ -368,11 +574,23 @@ def bench_ragged_window(torch, gqa, synth, steps, warmup):
     cells = int(sum(min(int(n), w) for n in lens.tolist()))
     nbytes = 2 * hkv * cells * d * 2 + 2 * B * hq * d * 2
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return dict(workload="gqa_decode_ragged_b32_hq8_hkv2_d64_w4096_bf16",
-                ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
-                frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
-                tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
-                per_call_ms=round(ms_call, 5), timing=f"{B2B}; {PER_CALL}")
+    res = dict(workload="gqa_decode_ragged_b32_hq8_hkv2_d64_w4096_bf16",
+               ms=round(ms, 5), bytes=nbytes, gbs=round(gbs, 2),
+               frac_of_hbm_peak=round(gbs / HBM_PEAK_GBS, 4),
+               tokens_per_s=round(B / (ms * 1e-3), 1), window_cells_read=cells,
+               per_call_ms=round(ms_call, 5), timing=f"{B2B}; {PER_CALL}",
+               traffic=measured_traffic("ragged"))
+    if cpu:
+        import oracle
+
+        del ks, vs
+        qn, kn, vn = _f64(q), _f64(k0), _f64(v0)
+        sl = lens.tolist()
+        res["cpu_baseline"] = _oracle_baseline(
+            lambda: oracle.decode(qn, kn, vn, seqlens=sl, window=w), nbytes, 1e9, "GB/s",
+            "the whole ragged sliding-window workload (B=32, Hq=8, Hkv=2, d=64, window 4096, "
+            "lengths in [1, 32768]) in fp64", budget_s=1.0)
+    return res
 
 
 def bench_small_f32(torch, gqa, synth, steps, warmup):
@@ -434,7 +652,7 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(r, budget_s=11.0):
+def cpu_baseline(r, budget_s=8.0):
     """The fp64 oracle as it stands, on the host cores, on the decode workload;
     plus one thread on batch row 0 (1/8 of the bytes), scaled to the whole."""
     import ctypes
@@ -483,6 +701,24 @@ def cpu_baseline(r, budget_s=11.0):
                                          "whole workload, whose rows are independent"})
 
 
+def run_leg(torch, gqa, synth, leg, steps, warmup):
+    """One leg alone, for counter runs (every library dispatch is this leg's)."""
+    if leg == "decode":
+        r = bench_decode(torch, gqa, synth, steps, warmup)
+        res = {"ms": round(r["ms"], 5)}
+    elif leg == "prefill":
+        res = bench_prefill(torch, gqa, synth, steps, warmup)
+    elif leg == "prefix":
+        res = bench_prefix(torch, gqa, synth, steps, warmup)
+    elif leg == "ring":
+        res = bench_ring(torch, gqa, synth, steps, warmup)
+    elif leg.startswith("sweep"):
+        res = bench_sweep(torch, gqa, synth, steps, warmup, hkvs=[int(leg[5:])])
+    else:
+        res = bench_ragged_window(torch, gqa, synth, steps, warmup)
+    print(json.dumps({"leg": leg, "result": res}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -491,7 +727,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--leg", choices=sorted(LEG_SOURCE), default=None,
+                    help="run one leg only (for hardware-counter runs)")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="print the per-leg traffic summary of counter runs under DIR")
     args = ap.parse_args()
+    if args.summarize_counters:
+        sys.stdout.write(summarize_counters(args.summarize_counters))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(decode and prefill shard over sequences or KV groups with no exchange, so "
@@ -504,6 +747,11 @@ def main():
     from gqa_kv_cache_02_amd import synth
 
     gqa.lib()
+    if args.leg is not None:
+        run_leg(torch, gqa, synth, args.leg, args.steps, args.warmup)
+        if args.copy_calibration:
+            copy_calibration(torch)
+        return
     r = bench_decode(torch, gqa, synth, args.steps, args.warmup)
     cfg = r["cfg"]
     gbs = r["nbytes"] / (r["ms"] * 1e-3) / 1e9
@@ -529,7 +777,7 @@ def main():
         "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic("decode"),
                      "bytes_per_launch": r["nbytes"],
                      "avg_launch_ms": round(r["avg_call_ms"], 5),
                      "min_launch_ms": round(r["min_call_ms"], 5),
@@ -541,12 +789,15 @@ def main():
     copy_gbs = hbm_copy_reference(torch)
     line["roofline"]["hbm_copy_reference_gbs"] = copy_gbs
     line["frac_of_measured_copy"] = round(gbs / copy_gbs, 4)
+    cpu = not args.no_cpu_baseline
     if not args.no_prefill:
-        line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3)
-        line["prefix_prefill"] = bench_prefix(torch, gqa, synth, max(10, args.steps // 10), 3)
-    line["ring_decode"] = bench_ring(torch, gqa, synth, max(20, args.steps // 2), 10)
-    line["decode_sweep"] = bench_sweep(torch, gqa, synth, max(20, args.steps // 2), 10)
-    line["ragged_window_decode"] = bench_ragged_window(torch, gqa, synth, max(20, args.steps // 2), 10)
+        line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3, cpu)
+        line["prefix_prefill"] = bench_prefix(torch, gqa, synth, max(10, args.steps // 10), 3,
+                                              cpu)
+    line["ring_decode"] = bench_ring(torch, gqa, synth, max(20, args.steps // 2), 10, cpu)
+    line["decode_sweep"] = bench_sweep(torch, gqa, synth, max(20, args.steps // 2), 10, cpu)
+    line["ragged_window_decode"] = bench_ragged_window(torch, gqa, synth,
+                                                       max(20, args.steps // 2), 10, cpu)
     line["small_f32_prefill"] = bench_small_f32(torch, gqa, synth, max(20, args.steps // 2), 10)
     if args.copy_calibration:
         copy_calibration(torch)
