@@ -64,6 +64,8 @@ def _load():
     L.gqa_decode_workspace_bytes.restype = sz
     L.gqa_decode.argtypes = [vp] * 5 + [i32] * 6 + [f32, i32, vp, sz, vp]
     L.gqa_decode.restype = ctypes.c_int
+    L.gqa_decode_no_alloc.argtypes = [vp] * 5 + [i32] * 6 + [f32, i32, vp]
+    L.gqa_decode_no_alloc.restype = ctypes.c_int
     L.gqa_decode_records.argtypes = [vp] * 5 + [i32] * 6 + [f32, i32, vp, sz, vp, vp]
     L.gqa_decode_records.restype = ctypes.c_int
     L.gqa_prefill_prefix.argtypes = [vp] * 7 + [i32] * 7 + [f32, i32, vp, sz, vp, vp]
@@ -260,6 +262,35 @@ def decode(q, k, v, *, seqlens=None, window=None, scale=None, out=None, workspac
         rc = L.gqa_decode(*args, _stream(dev))
     if rc:
         raise GQAError(rc, "gqa_decode")
+    return out
+
+
+def decode_no_alloc(q, k, v, *, seqlens=None, window=None, scale=None, out=None):
+    """decode() without a workspace: the library keeps the split partials in
+    its own device array (one per GPU), so the call allocates nothing when
+    ``out`` and ``seqlens`` are given as device tensors.  Calls that may
+    overlap in time on one GPU share that array and must be serialised."""
+    L = _load()
+    if q.dim() != 3 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be 3-D and k, v 4-D")
+    B, hq, d = q.shape
+    hkv, C = k.shape[1], k.shape[2]
+    if k.shape != (B, hkv, C, d) or v.shape != k.shape:
+        raise ValueError(f"k/v shape {tuple(k.shape)}/{tuple(v.shape)} does not match q {tuple(q.shape)}")
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, q.dtype, dev)
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=q.dtype, device=dev)
+    _check_tensor("out", out, q.dtype, dev)
+    if out.shape != (B, hq, d):
+        raise ValueError("out must be [B,Hq,d]")
+    sl = _seq(seqlens, B, dev)
+    sc = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    rc = L.gqa_decode_no_alloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(sl), B, C, hq, hkv, d,
+                               _win(window), sc, _dt(q.dtype), _stream(dev))
+    if rc:
+        raise GQAError(rc, "gqa_decode_no_alloc")
     return out
 
 

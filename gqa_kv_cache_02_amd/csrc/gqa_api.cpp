@@ -18,6 +18,9 @@
 #include "gqa.h"
 #include "gqa_internal.hpp"
 
+static_assert(gqa::kDecodeScratchBytes == GQA_DECODE_SCRATCH_BYTES,
+              "the header states the no-allocation decode's array size");
+
 namespace {
 
 using gqa::Problem;
@@ -168,7 +171,7 @@ int decode_impl(const void *q, const void *k, const void *v, void *out, const in
                 int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t d, int32_t window,
                 float scale, int32_t dtype, void *workspace, size_t workspace_bytes,
                 int32_t *records, bool want_records, void *stream,
-                const CacheExtra &x = CacheExtra()) {
+                const CacheExtra &x = CacheExtra(), bool use_scratch = false) {
     int rc = check_scalars(Hq, Hkv, d, window, scale, dtype);
     if (rc)
         return rc;
@@ -212,7 +215,13 @@ int decode_impl(const void *q, const void *k, const void *v, void *out, const in
             return GQA_ERR_SHAPE;
         // the workspace holds split partials only: without a split it is
         // never touched and may be NULL
-        if (plan.nsplit > 1) {
+        if (plan.nsplit > 1 && use_scratch) {
+            // the library's own array instead of a caller's workspace
+            if (plan.bytes > gqa::kDecodeScratchBytes)
+                return GQA_ERR_WORKSPACE;
+            if (gqa::decode_scratch(s, &workspace) != hipSuccess)
+                return GQA_ERR_HIP;
+        } else if (plan.nsplit > 1) {
             if (!workspace)
                 return GQA_ERR_NULL;
             if (!aligned(workspace, 256))
@@ -266,6 +275,13 @@ int gqa_decode(const void *q, const void *k_cache, const void *v_cache, void *ou
                size_t workspace_bytes, void *stream) {
     return decode_impl(q, k_cache, v_cache, out, seqlens, B, C, Hq, Hkv, d, window, scale, dtype,
                        workspace, workspace_bytes, nullptr, false, stream);
+}
+
+int gqa_decode_no_alloc(const void *q, const void *k_cache, const void *v_cache, void *out,
+                        const int32_t *seqlens, int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
+                        int32_t d, int32_t window, float scale, int32_t dtype, void *stream) {
+    return decode_impl(q, k_cache, v_cache, out, seqlens, B, C, Hq, Hkv, d, window, scale, dtype,
+                       nullptr, 0, nullptr, false, stream, CacheExtra(), true);
 }
 
 int gqa_decode_records(const void *q, const void *k_cache, const void *v_cache, void *out,

@@ -44,6 +44,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "gqa_common.hpp"
 #include "gqa_internal.hpp"
@@ -580,6 +581,46 @@ __global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
         rec[0] = static_cast<int>(row % a.Hq) / a.r;
         rec[1] = rl; rec[2] = rh; rec[3] = cnt; rec[4] = x;
     }
+}
+
+// The split workspace of gqa_decode_no_alloc, for callers that cannot
+// allocate.  Every GPU holds its own copy until the process ends; its
+// contents on entry never matter (each call writes the partials it reads).
+// In host code `scratch` names a host-side stand-in, not device memory: the
+// kernels are only ever given the address hipGetSymbolAddress returns.
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+hipError_t decode_scratch(hipStream_t stream, void **ptr) {
+    int dev = 0;
+    hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        if ((e = hipGetDevice(&cur)) != hipSuccess)
+            return e;
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return e;
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess)
+                e = e2;
+        }
+        if (e != hipSuccess)
+            return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
 }
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }

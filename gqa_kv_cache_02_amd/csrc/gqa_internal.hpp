@@ -59,6 +59,16 @@ constexpr int kDecodeCUs = 256; // compute units of the MI355X the decode plan t
 
 DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window);
 
+// Library-owned split workspace of the no-allocation decode entry point: a
+// file-scope device array of this many bytes on each GPU the library runs on.
+// The split plan keeps at most two workgroups of at most 16 heads per CU, so
+// a call's partials hold at most 16 * 512 rows of (d + 5) * 4 bytes: 4.4 MB
+// at d = 128.
+constexpr size_t kDecodeScratchBytes = size_t{8} << 20;
+// Device address of that array on the GPU of `stream` (looked up once per
+// device, with that device current).
+hipError_t decode_scratch(hipStream_t stream, void **ptr);
+
 hipError_t launch_generic(const Problem &p, hipStream_t stream);
 hipError_t launch_decode_split(const Problem &p, const DecodePlan &plan, void *workspace,
                                hipStream_t stream);

@@ -41,7 +41,8 @@
  *   - Preconditions that live in device memory are NOT checked (checking would
  *     need a synchronisation): 0 <= seqlens[b] <= T for prefill and
  *     0 <= seqlens[b] <= C for decode (see each entry point for the rest).
- *   - Calls are thread-safe; the library holds no mutable state.
+ *   - Calls are thread-safe; the library holds no mutable state (except the
+ *     device array of gqa_decode_no_alloc, see there).
  */
 #ifndef GQA_H
 #define GQA_H
@@ -134,6 +135,25 @@ int gqa_decode(const void *q, const void *k_cache, const void *v_cache, void *ou
                const int32_t *seqlens, int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
                int32_t d, int32_t window, float scale, int32_t dtype, void *workspace,
                size_t workspace_bytes, void *stream);
+
+/*
+ * Decode that allocates nothing and takes no workspace: for callers that
+ * cannot allocate device memory at call time (work being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc).  It runs the
+ * kernels of gqa_decode with their split partials kept in a library-owned
+ * device array of GQA_DECODE_SCRATCH_BYTES, one per GPU the library runs on
+ * (set up on the first call on that GPU, held until the process ends).
+ * Arguments, results and refusals are those of gqa_decode; a split plan whose
+ * partials would not fit the array is refused with GQA_ERR_WORKSPACE (the
+ * plans of every decode shape need at most about 4.4 MB).  All calls on one GPU
+ * share its array, which keeps the last call's contents (no call depends on
+ * them): calls that may overlap in time on one GPU -- other streams or other
+ * host threads -- race, and the caller must serialise them.
+ */
+#define GQA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+int gqa_decode_no_alloc(const void *q, const void *k_cache, const void *v_cache, void *out,
+                        const int32_t *seqlens, int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
+                        int32_t d, int32_t window, float scale, int32_t dtype, void *stream);
 
 /*
  * Index-set records: the same kernels, instantiated to also write, for every

@@ -1,0 +1,95 @@
+"""gqa_decode_no_alloc (the decode entry point that allocates nothing and
+keeps its split partials in the library's own device array) against
+gqa_decode (caller's workspace) and the fp64 oracle, through the C-ABI:
+two calls in a row on one GPU, the second with a smaller input, so the
+second call runs over what the first left in the shared array."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gqa_kv_cache_02_amd as gqa
+import oracle
+from gqa_kv_cache_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2
+F32_TOL = 1e-5
+DEV = "cuda"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gqa.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _no_alloc_call(q, k, v, out, seqlens, window):
+    """The raw C call: device pointers, sizes, the current stream."""
+    B, hq, d = q.shape
+    hkv, C = k.shape[1], k.shape[2]
+    dt = 1 if q.dtype == torch.bfloat16 else 0
+    w = -1 if window is None else window
+    stream = torch.cuda.current_stream().cuda_stream
+    return gqa.lib().gqa_decode_no_alloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                         out.data_ptr(), seqlens.data_ptr(), B, C, hq, hkv, d,
+                                         w, 1.0 / math.sqrt(d), dt, stream)
+
+
+# (B, C, Hq, Hkv, d, window, dtype, seed, lengths): the headline decode
+# shape (4 splits), then smaller inputs: MQA with 16 splits over a short
+# cache, a ragged window at d = 64, one row without a split, and fp32 (the
+# generic kernel, no partials at all)
+CASES = [
+    (8, 8000, 32, 8, 128, None, torch.bfloat16, 61, None),
+    (4, 3000, 8, 1, 128, None, torch.bfloat16, 62, [3000, 2999, 700, 1]),
+    (6, 5000, 8, 2, 64, 1000, torch.bfloat16, 63, [5000, 17, 0, 1001, 4321, 999]),
+    (2, 100, 4, 2, 64, None, torch.bfloat16, 64, [100, 50]),
+    (2, 90, 4, 2, 8, 7, torch.float32, 65, [90, 3]),
+]
+
+
+def _run_pair(first, second):
+    for B, C, hq, hkv, d, w, dt, seed, lens in (first, second):
+        q, k, v = synth.decode_inputs(B, C, hq, hkv, d, dt, seed, DEV)
+        lens = [C] * B if lens is None else lens
+        sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+        out = torch.full((B, hq, d), 7.0, dtype=dt, device=DEV)
+        assert _no_alloc_call(q, k, v, out, sl, w) == 0
+        ref_ws = gqa.decode(q, k, v, seqlens=sl, window=w)
+        torch.cuda.synchronize()
+        # the same kernels and plan as gqa_decode: bit for bit its output
+        assert torch.equal(out, ref_ws), (B, C, hq, hkv, d, w)
+        ref, _, _ = oracle.decode(_np(q), _np(k), _np(v), seqlens=lens, window=w)
+        tol = BF16_TOL if dt == torch.bfloat16 else F32_TOL
+        assert float(np.max(np.abs(_np(out) - ref))) <= tol
+
+
+@pytest.mark.parametrize("i", range(len(CASES) - 1))
+def test_two_calls_in_a_row_second_smaller(i):
+    _run_pair(CASES[0] if i == 0 else CASES[i], CASES[i + 1])
+
+
+def test_binding_and_refusals():
+    B, C, hq, hkv, d = 2, 600, 8, 2, 128
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 66, DEV)
+    out = gqa.decode_no_alloc(q, k, v, seqlens=[600, 300], window=200)
+    ref = gqa.decode(q, k, v, seqlens=[600, 300], window=200)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+    # refusals come back before anything is launched, output untouched
+    keep = torch.full((B, hq, d), 3.0, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(gqa.GQAError) as e:
+        gqa.decode_no_alloc(q, k, v, window=0, out=keep)
+    assert e.value.status == 3
+    torch.cuda.synchronize()
+    assert (keep == 3.0).all()
