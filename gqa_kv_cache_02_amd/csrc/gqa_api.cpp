@@ -211,7 +211,7 @@ int decode_impl(const void *q, const void *k, const void *v, void *out, const in
         if (!fast_aligned(q, k, v, out) || !cand_aligned)
             return GQA_ERR_ALIGN;
         const gqa::DecodePlan plan = gqa::plan_decode(B, C, Hq, Hkv, d, window);
-        if (B > kMaxGridYZ || (int64_t)Hkv * plan.nhc > kMaxGridYZ)
+        if (!gqa::decode_grid_ok(B, Hkv, plan))
             return GQA_ERR_SHAPE;
         // the workspace holds split partials only: without a split it is
         // never touched and may be NULL

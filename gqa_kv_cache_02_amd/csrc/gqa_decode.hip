@@ -65,6 +65,7 @@ struct DecodeArgs {
     float *lse_part;    // [B, Hq, nsplit]
     int32_t *rec_part;  // [B, Hq, nsplit, 4] (record instantiation only)
     int C, Hq, Hkv, window, r, nhc, nsplit, chunk;
+    int units; // B * Hkv * nhc
     float scale_log2;
     // kExt only
     const uint16_t *knew; // [B, Hkv, D] candidate key (nullable)
@@ -114,10 +115,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     const int hl = lane & 15; // head within the 16-head chunk (MFMA column)
     const int qg = lane >> 4; // lane group (MFMA k/row group)
 
-    const int b = blockIdx.z;
-    const int g = blockIdx.y / a.nhc;
-    const int hc = blockIdx.y % a.nhc;
-    const int split = blockIdx.x;
+    // One-dimensional grid.  Workgroups are dispatched to the 8 XCDs in turn
+    // (linear id mod 8), so all splits of a (b, g, head chunk) unit u run on
+    // XCD u mod 8, where the merge kernel's workgroup for u runs too: the
+    // merge then finds the partials in that XCD's cache.
+    const int ns_grid = a.nsplit > 0 ? a.nsplit : 1;
+    const int wid = static_cast<int>(blockIdx.x);
+    const int split = (wid >> 3) % ns_grid;
+    const int unit = ((wid >> 3) / ns_grid) * 8 + (wid & 7);
+    if (unit >= a.units)
+        return; // the grid is rounded up to whole groups of 8 units
+    const int b = unit / (a.Hkv * a.nhc);
+    const int g = (unit / a.nhc) % a.Hkv;
+    const int hc = unit % a.nhc;
     const int h0 = g * a.r + hc * kDecodeHeads;
     const int nh = min(kDecodeHeads, a.r - hc * kDecodeHeads);
     const int64_t row0 = (int64_t)b * a.Hq + h0; // first (b, h) row of this workgroup
@@ -482,20 +492,29 @@ struct MergeArgs {
     const int32_t *seqlens;
     uint16_t *out;
     int32_t *records;
-    int B, C, Hq, r, window, nsplit, chunk;
+    int B, C, Hq, Hkv, nhc, r, window, nsplit, chunk;
 };
 
-// One thread per 4 output features of a row (b, h) with more than one chunk:
-// out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max_s lse_s).
+// Workgroup u merges the rows of unit u (batch row b, KV group g, head chunk
+// hc: up to 16 query heads), on the XCD where that unit's splits ran (see
+// decode_kernel).  One thread per 4 output features of a row with more than
+// one chunk: out = sum_s w_s o_s / sum_s w_s with w_s = 2^(lse_s - max lse).
+template <int D> constexpr int merge_threads() { return kDecodeHeads * (D / 4); }
+
 template <int D, bool kRecord>
-__global__ __launch_bounds__(256) void decode_merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(merge_threads<D>()) void decode_merge_kernel(MergeArgs a) {
     constexpr int Q4 = D / 4;
-    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (int64_t)a.B * a.Hq * Q4)
+    const int unit = static_cast<int>(blockIdx.x);
+    const int b = unit / (a.Hkv * a.nhc);
+    const int g = (unit / a.nhc) % a.Hkv;
+    const int hc = unit % a.nhc;
+    const int h0 = g * a.r + hc * kDecodeHeads;
+    const int nh = min(kDecodeHeads, a.r - hc * kDecodeHeads);
+    const int hl = static_cast<int>(threadIdx.x) / Q4;
+    if (hl >= nh)
         return;
-    const int64_t row = idx / Q4;
-    const int c4 = static_cast<int>(idx % Q4) * 4;
-    const int b = static_cast<int>(row / a.Hq);
+    const int64_t row = (int64_t)b * a.Hq + h0 + hl;
+    const int c4 = (static_cast<int>(threadIdx.x) % Q4) * 4;
     const float *lse = a.lse_part + row * a.nsplit;
     const float *op = a.o_part + row * a.nsplit * D + c4;
     // Partials are loaded in unrolled chunks of kChunk splits, every load of
@@ -661,6 +680,18 @@ DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window) {
     return p;
 }
 
+// The split kernel's grid is one-dimensional: units rounded up to groups of
+// 8, times the splits, workgroups of 256 work-items; the merge kernel's is
+// one workgroup of up to 512 work-items per unit.  Both totals must fit a
+// 32-bit count.
+bool decode_grid_ok(int B, int Hkv, const DecodePlan &plan) {
+    const int64_t units = (int64_t)B * Hkv * plan.nhc;
+    const int64_t ns = plan.nsplit > 0 ? plan.nsplit : 1;
+    const int64_t wgs = (units + 7) / 8 * 8 * ns;
+    return units <= INT_MAX && wgs * 256 <= (int64_t)UINT32_MAX &&
+           units * merge_threads<128>() <= (int64_t)UINT32_MAX;
+}
+
 template <int D, bool kRecord, bool kExt>
 static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, hipStream_t s) {
     // no workspace without a split (every row finishes in the split kernel)
@@ -677,25 +708,27 @@ static hipError_t launch_d(const Problem &p, const DecodePlan &plan, void *ws, h
     a.rec_part = w ? reinterpret_cast<int32_t *>(w + plan.rec_off) : nullptr;
     a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
     a.r = p.Hq / p.Hkv; a.nhc = plan.nhc; a.nsplit = plan.nsplit; a.chunk = plan.chunk;
+    a.units = p.B * p.Hkv * plan.nhc;
     a.scale_log2 = p.scale * kLog2e;
     a.knew = static_cast<const uint16_t *>(p.knew);
     a.vnew = static_cast<const uint16_t *>(p.vnew);
     a.kw = static_cast<uint16_t *>(p.kw);
     a.vw = static_cast<uint16_t *>(p.vw);
     a.ring = p.ring ? 1 : 0;
-    // at least one split so that empty rows still get their zero output
-    dim3 grid(plan.nsplit > 0 ? plan.nsplit : 1, p.Hkv * plan.nhc, p.B);
-    decode_kernel<D, kRecord, kExt><<<grid, 256, 0, s>>>(a);
+    // at least one split so that empty rows still get their zero output;
+    // units in whole groups of 8 (one per XCD)
+    const int64_t ns_grid = plan.nsplit > 0 ? plan.nsplit : 1;
+    const int64_t wgs = ((int64_t)a.units + 7) / 8 * 8 * ns_grid;
+    decode_kernel<D, kRecord, kExt><<<dim3((unsigned)wgs), 256, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || plan.nsplit <= 1)
         return e; // every row finished inside the split kernel
     MergeArgs m;
     m.o_part = a.o_part; m.lse_part = a.lse_part; m.rec_part = a.rec_part;
     m.seqlens = p.seqlens; m.out = a.out; m.records = p.records;
-    m.B = p.B; m.C = p.C; m.Hq = p.Hq; m.r = a.r; m.window = p.window;
-    m.nsplit = plan.nsplit; m.chunk = plan.chunk;
-    const int64_t threads = (int64_t)p.B * p.Hq * (D / 4);
-    decode_merge_kernel<D, kRecord><<<dim3((unsigned)((threads + 255) / 256)), 256, 0, s>>>(m);
+    m.B = p.B; m.C = p.C; m.Hq = p.Hq; m.Hkv = p.Hkv; m.nhc = plan.nhc; m.r = a.r;
+    m.window = p.window; m.nsplit = plan.nsplit; m.chunk = plan.chunk;
+    decode_merge_kernel<D, kRecord><<<dim3((unsigned)a.units), merge_threads<D>(), 0, s>>>(m);
     return hipGetLastError();
 }
 

@@ -58,6 +58,7 @@ constexpr int kDecodeHeads = 16;
 constexpr int kDecodeCUs = 256; // compute units of the MI355X the decode plan targets
 
 DecodePlan plan_decode(int B, int C, int Hq, int Hkv, int d, int window);
+bool decode_grid_ok(int B, int Hkv, const DecodePlan &plan);
 
 // Library-owned split workspace of the no-allocation decode entry point: a
 // file-scope device array of this many bytes on each GPU the library runs on.

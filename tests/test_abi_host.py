@@ -129,7 +129,7 @@ def test_refusals_decode():
     assert _decode(C=8000, wsb=need - 1) == WORKSPACE
     assert _decode(C=8000, ws=None) == NULL
     assert _decode(C=8000, ws=ctypes.c_void_p(4096 + 16)) == ALIGN
-    assert _decode(B=70000) == SHAPE
+    assert _decode(B=20_000_000) == SHAPE  # more workgroups than a 32-bit grid holds
     assert _decode(B=0, q=None, k=None, v=None, out=None) == OK
     assert gqa.lib().gqa_decode_records(P, P, P, P, None, 2, 64, 8, 2, 128, -1, 0.5, 1, P,
                                         1 << 30, None, None) == NULL
