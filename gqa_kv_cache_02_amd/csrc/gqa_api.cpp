@@ -52,6 +52,9 @@ int check_scalars(int32_t Hq, int32_t Hkv, int32_t d, int32_t window, float scal
 // Element counts of every array must fit in int64 (kernels index with int64).
 int check_sizes(int64_t B, int64_t Hq, int64_t Hkv, int64_t T, int64_t C, int64_t d,
                 int32_t dtype) {
+    // every kernel counts cells in int, with room past C for a tile's reach
+    if (C > GQA_MAX_CELLS)
+        return GQA_ERR_SHAPE;
     int64_t x;
     const int64_t es = elem_size(dtype);
     if (!mul_ok(B, Hq, &x) || !mul_ok(x, T, &x) || !mul_ok(x, d, &x) || !mul_ok(x, es, &x))

@@ -35,6 +35,8 @@
  *     which need q, k_cache, v_cache, out (and k_new, v_new) 16-byte
  *     aligned; such a call with any of them misaligned is refused with
  *     GQA_ERR_ALIGN (it is never rerouted to another kernel).
+ *   - C (cache cells) is at most GQA_MAX_CELLS = 2^30 for every entry point
+ *     (else GQA_ERR_SHAPE): the kernels count cells in 32-bit integers.
  *   - Every argument check happens on the host before anything is enqueued;
  *     on any error nothing is launched and out is left untouched (a failed
  *     call never half-advances anything, as the pages require of the cache).
@@ -54,6 +56,9 @@
 extern "C" {
 #endif
 
+/* Largest cache length C (cells) any entry point accepts. */
+#define GQA_MAX_CELLS ((int32_t)1 << 30)
+
 typedef enum {
     GQA_OK = 0,
     GQA_ERR_NULL = 1,        /* a required pointer is NULL                         */
@@ -61,7 +66,8 @@ typedef enum {
     GQA_ERR_ZERO_WINDOW = 3, /* window == 0                                        */
     GQA_ERR_HEAD_DIM = 4,    /* d < 1 or d > 256                                   */
     GQA_ERR_DTYPE = 5,       /* dtype is not GQA_F32 or GQA_BF16                   */
-    GQA_ERR_SHAPE = 6,       /* negative B/T/C, T > C, or a grid limit exceeded    */
+    GQA_ERR_SHAPE = 6,       /* negative B/T/C, T > C, C > GQA_MAX_CELLS, or a
+                                grid limit exceeded                                */
     GQA_ERR_OVERFLOW = 7,    /* an element count or byte size overflows int64      */
     GQA_ERR_WORKSPACE = 8,   /* workspace smaller than gqa_decode_workspace_bytes  */
     GQA_ERR_ALIGN = 9,       /* a pointer is misaligned: to its element size, or to

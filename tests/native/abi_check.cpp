@@ -81,6 +81,9 @@ int refusals() {
     EXPECT(gqa_prefill(P, P, P, P, nullptr, B, C + 1, C, Hq, Hkv, d, -1, 0.5f, GQA_BF16,
                        nullptr) == GQA_ERR_SHAPE,
            "T > C is not refused");
+    EXPECT(gqa_decode(P, P, P, P, nullptr, B, GQA_MAX_CELLS + 1, Hq, Hkv, d, -1, 0.5f,
+                      GQA_BF16, P, 1 << 20, nullptr) == GQA_ERR_SHAPE,
+           "a cache longer than GQA_MAX_CELLS is not refused");
     const size_t need = gqa_decode_workspace_bytes(B, C, Hq, Hkv, d, -1, GQA_BF16);
     EXPECT(need > 0, "no workspace for the split decode");
     EXPECT(gqa_decode(P, P, P, P, nullptr, B, C, Hq, Hkv, d, -1, 0.5f, GQA_BF16, P, need - 1,

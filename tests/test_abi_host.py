@@ -100,6 +100,7 @@ def test_refusals_prefill():
     assert _prefill(T=5, C=4) == SHAPE
     assert _prefill(B=-1) == SHAPE
     assert _prefill(B=2 ** 31 - 1, T=2 ** 30, C=2 ** 30, d=256) == OVERFLOW
+    assert _prefill(T=4, C=2 ** 30 + 1) == SHAPE  # past GQA_MAX_CELLS
     assert _prefill(q=None) == NULL
     assert _prefill(out=None) == NULL
     assert _prefill(k=P_ODD) == ALIGN
@@ -130,6 +131,10 @@ def test_refusals_decode():
     assert _decode(C=8000, ws=None) == NULL
     assert _decode(C=8000, ws=ctypes.c_void_p(4096 + 16)) == ALIGN
     assert _decode(B=20_000_000) == SHAPE  # more workgroups than a 32-bit grid holds
+    # cells past GQA_MAX_CELLS: refused, no kernel, no workspace
+    assert _decode(C=2 ** 30 + 1) == SHAPE
+    assert gqa.lib().gqa_decode_kernel(2, 2 ** 30 + 1, 8, 2, 128, -1, 1) == 0
+    assert gqa.lib().gqa_decode_workspace_bytes(2, 2 ** 30 + 1, 8, 2, 128, -1, 1) == 0
     assert _decode(B=0, q=None, k=None, v=None, out=None) == OK
     assert gqa.lib().gqa_decode_records(P, P, P, P, None, 2, 64, 8, 2, 128, -1, 0.5, 1, P,
                                         1 << 30, None, None) == NULL
@@ -195,6 +200,7 @@ def test_refusals_prefill_prefix():
     assert _prefix(Hq=6, Hkv=4) == HEADS
     assert _prefix(window=0) == ZERO_WINDOW
     assert _prefix(Tq=9, C=8) == SHAPE          # more query rows than cells
+    assert _prefix(Tq=4, C=2 ** 30 + 1) == SHAPE  # past GQA_MAX_CELLS
     assert _prefix(q=None) == NULL
     assert _prefix(qlens=ctypes.c_void_p(4098)) == ALIGN
     assert _prefix(segs=ctypes.c_void_p(4098)) == ALIGN
@@ -218,6 +224,7 @@ def test_refusals_decode_cache():
     assert _dcache(window=-1) == SHAPE           # a rolling cache needs a window
     assert _dcache(window=65) == SHAPE           # ... no longer than the capacity
     assert _dcache(window=0) == ZERO_WINDOW
+    assert _dcache(C=2 ** 30 + 1, window=4) == SHAPE  # past GQA_MAX_CELLS
     assert _dcache(kn=P) == NULL                 # the key without the value
     assert _dcache(vn=P) == NULL
     assert _dcache(kn=P_ODD, vn=P) == ALIGN
