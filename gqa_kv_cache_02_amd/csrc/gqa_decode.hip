@@ -418,7 +418,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     // would wait for the loads in flight) sits between tiles.
     bf16x8 ka0[2][KS], ka1[2][KS];
     u32x4 vr0[VIT], vr1[VIT];
-    int j0 = c_lo + wave * kDecodeTile;
+    // j0 is the same in every lane of a wavefront; saying so keeps it in
+    // scalar registers
+    int j0 = __builtin_amdgcn_readfirstlane(c_lo + wave * kDecodeTile);
     if (j0 <= c_hi)
         load_tile(j0, ka0, vr0);
     while (j0 <= c_hi) {
