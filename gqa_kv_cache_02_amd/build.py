@@ -4,11 +4,19 @@
 
 Every translation unit is compiled for gfx950 only, with packed-fp32 VALU
 instructions disabled, then linked into gqa_kv_cache_02_amd/libgqa.so.
+
+The compiler's resource report for each HIP file is checked: every device
+function it lists must be a kernel (nothing compiled out of line into a
+called function) and use no scratch memory.  A kernel whose tile math was
+split into called functions reached its operands through pointers into
+scratch; two such prefill variants faulted the GPU, so the build refuses
+that form outright.
 """
 from __future__ import annotations
 
 import concurrent.futures as cf
 import os
+import re
 import subprocess
 import sys
 
@@ -29,16 +37,47 @@ FLAGS = [
 ]
 
 
+REMARK = "-Rpass-analysis=kernel-resource-usage"
+_KERNEL = re.compile(r"^_ZN3gqa\d+[a-z0-9_]*_kernelI")
+
+
+def resource_violations(report: str) -> list[str]:
+    """Device functions in a compiler resource report that are not kernels,
+    or that use scratch memory.  `report` is hipcc's stderr with REMARK on."""
+    out = []
+    name = None
+    for ln in report.splitlines():
+        m = re.search(r"Function Name: (\S+)", ln)
+        if m:
+            name = m.group(1)
+            if not _KERNEL.match(name):
+                out.append(f"{name}: a called device function (tile math compiled out of line)")
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", ln)
+        if m and name is not None and int(m.group(1)) > 0:
+            out.append(f"{name}: {m.group(1)} bytes of scratch per lane")
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    hip = src.endswith(".hip")
+    # (no source excerpts under the remarks: they would bury real warnings)
+    extra = [REMARK, "-fno-caret-diagnostics"] if hip else []
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
+    if hip:
+        bad = resource_violations(res.stderr)
+        if bad:
+            raise RuntimeError(f"{src}: every kernel must run without calls and without "
+                               "scratch:\n  " + "\n  ".join(bad))
     # hipcc's host pass does not know the packed-fp32 target feature; that
-    # warning is expected, anything else is shown.
-    noise = "'-packed-fp32-ops' is not a recognized feature"
-    msgs = [ln for ln in res.stderr.splitlines() if ln.strip() and noise not in ln]
+    # warning is expected, anything else (but the resource report) is shown.
+    noise = ("'-packed-fp32-ops' is not a recognized feature", REMARK)
+    msgs = [ln for ln in res.stderr.splitlines()
+            if ln.strip() and not any(n in ln for n in noise)]
     if msgs:
         print(f"[{src}]\n" + "\n".join(msgs), file=sys.stderr)
     return obj
