@@ -6,12 +6,13 @@
 // "Share key/value heads and make context explicit", "Intersect the window
 // with the context already permitted", and "Extend the existing full and
 // cached attention paths" for the query's position).  That range is cut into
-// chunks of `chunk` keys counted from lo; workgroup (split, g, b) takes chunk
-// `split` for ALL query heads of group g at once (up to 16 per workgroup), so
-// every K/V cell is fetched from HBM once per group and feeds the r heads that
-// share it -- the saving GQA exists for ("How do you implement grouped query
-// attention (GQA)?", Step 4: the cache stores G heads and is repeated on
-// read; here the repeat never materialises).
+// chunks of `chunk` keys counted from lo; a workgroup takes one chunk of one
+// unit (batch row b, KV group g, up to 16 of the group's query heads) for all
+// of the unit's heads at once, so every K/V cell is fetched from HBM once per
+// group and feeds the r heads that share it -- the saving GQA exists for
+// ("How do you implement grouped query attention (GQA)?", Step 4: the cache
+// stores G heads and is repeated on read; here the repeat never
+// materialises).
 //
 // Inside a workgroup, 4 wavefronts take interleaved 32-key tiles; each
 // wavefront prefetches its next tile while it computes the current one.
