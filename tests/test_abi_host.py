@@ -219,6 +219,45 @@ def test_refusals_prefill_prefix():
     assert _prefix(**big, ws=ctypes.c_void_p(4096 + 16), wsb=need) == ALIGN
 
 
+def _prefix_plan(B, T, C, hq, hkv, window):
+    """The key-range plan of queries against a cached prefix, restated: with
+    fewer than 256 blocks (8 wavefronts: heads x 32-row blocks) and at least 8
+    tiles of 64 keys, the key range is cut over ns workgroups while
+    blocks x ns stays under 256 and every split keeps 4 tiles.  Returns
+    (nsplit, workspace bytes)."""
+    r = hq // hkv
+    hpw = 8
+    while r % hpw:
+        hpw //= 2
+    rb = 8 // hpw
+    units = -(-T // (32 * rb)) * B * hkv * (r // hpw)
+    elig = window if 0 < window < C else C
+    mt = min(-(-C // 64), (elig + 32 * rb) // 64 + 2)
+    if not (0 < units < 256 and mt >= 8):
+        return 1, 0
+    ns = min(-(-256 // units), mt // 4)
+    if ns <= 1:
+        return 1, 0
+    tps = -(-mt // ns)
+    ns = -(-mt // tps)
+    rows = ns * B * T * hq
+    a = lambda x: (x + 255) // 256 * 256
+    return ns, a(rows * 128 * 4) + a(rows * 4) + a(rows * 16)
+
+
+def test_prefix_plan_splits():
+    L = gqa.lib()
+    for B, T, C, hq, hkv in ((1, 512, 4096, 32, 8), (2, 64, 700, 8, 2), (2, 64, 2100, 8, 2),
+                             (1, 4096, 4096, 32, 8), (2, 64, 2000, 4, 4), (2, 64, 2000, 6, 2),
+                             (1, 16, 30000, 64, 8), (3, 200, 5000, 16, 16), (1, 1, 9000, 8, 1)):
+        for w in (-1, 64, 700, 1200, 3000):
+            ns, want = _prefix_plan(B, T, C, hq, hkv, w)
+            got = L.gqa_prefill_prefix_workspace_bytes(B, T, C, hq, hkv, 128, w, 1)
+            assert got == want, (B, T, C, hq, hkv, w, ns)
+    # the chunked-prefill workload: 64 blocks, 4 splits of 16 tiles
+    assert _prefix_plan(1, 512, 4096, 32, 8, -1)[0] == 4
+
+
 def test_refusals_decode_cache():
     assert _dcache(ring=2) == SHAPE
     assert _dcache(window=-1) == SHAPE           # a rolling cache needs a window

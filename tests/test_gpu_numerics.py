@@ -89,6 +89,29 @@ def test_moving_maximum_prefill_and_decode(d, rate):
 
 
 @pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rate", [0.2, 1.5])
+def test_moving_maximum_split_prefix(d, rate):
+    # queries against a longer cache, with and without a window: each block's
+    # key range is cut over several workgroups (partials in the workspace,
+    # merged by the second kernel) whose log-sum-exps differ by hundreds to
+    # thousands
+    B, C, hq, hkv, Tq = 2, 2100, 8, 2, 64
+    q, k, v = _ramp_inputs(B, C, C, hq, hkv, d, rate, 6050 + d)
+    seqlens = [2100, 1500]
+    pq = torch.stack([q[b, :, seqlens[b] - Tq:seqlens[b]] for b in range(B)]).contiguous()
+    for w in (None, 1200):
+        assert gqa.prefill_prefix_workspace_bytes(B, Tq, C, hq, hkv, d, w) > 0  # the split path
+        pout = gqa.prefill_prefix(pq, k, v, seqlens=torch.tensor(seqlens, dtype=torch.int32,
+                                                                 device=DEV),
+                                  qlens=torch.tensor([Tq, Tq], dtype=torch.int32, device=DEV),
+                                  window=w)
+        torch.cuda.synchronize()
+        pref, _, _ = oracle.attend_prefix(_np(pq), _np(k), _np(v), seqlens=seqlens,
+                                          qlens=[Tq, Tq], window=w)
+        assert float(np.max(np.abs(_np(pout) - pref))) <= TOL, ("split prefix", d, rate, w)
+
+
+@pytest.mark.parametrize("d", [64, 128])
 def test_single_dominant_key(d):
     # one key per KV group scores far above all others: the output is that
     # key's value row (the softmax is one-hot to fp32 precision)
