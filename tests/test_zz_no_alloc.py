@@ -93,3 +93,33 @@ def test_binding_and_refusals():
     assert e.value.status == 3
     torch.cuda.synchronize()
     assert (keep == 3.0).all()
+
+
+def test_replay_in_a_graph():
+    # code under graph capture is what the entry point is for: the captured
+    # launches use the library's array, and every replay (with new queries
+    # written into the captured buffer and eager work in between) equals an
+    # eager gqa_decode on the same inputs
+    B, C, hq, hkv, d, w = 4, 3000, 16, 4, 128, 1000
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 67, DEV)
+    sl = torch.tensor([3000, 2000, 999, 1], dtype=torch.int32, device=DEV)
+    out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=DEV)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture
+        assert _no_alloc_call(q, k, v, out, sl, w) == 0
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rc = _no_alloc_call(q, k, v, out, sl, w)
+    assert rc == 0
+    torch.cuda.synchronize()
+    for i in range(4):
+        q.copy_(synth.randn((B, hq, d), 6800 + i, torch.bfloat16, DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = gqa.decode(q, k, v, seqlens=sl, window=w)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {i} differs from the eager call"
