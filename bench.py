@@ -652,7 +652,7 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(r, budget_s=8.0):
+def cpu_baseline(r, budget_s=12.0):
     """The fp64 oracle as it stands, on the host cores, on the decode workload;
     plus one thread on batch row 0 (1/8 of the bytes), scaled to the whole."""
     import ctypes
