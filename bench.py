@@ -32,6 +32,10 @@ Prints ONE JSON line.
   prefix_prefill queries against a cached prefix: the last 512 cells of a
                  4096-cell sequence as new rows (B=1, Hq=32, Hkv=8, d=128):
                  TFLOP/s of the permitted pairs against 2.5 PFLOP/s.
+  packed_prefill packed segments: sequences of 64..1024 cells back to back in
+                 one 4096-cell causal row (B=1, Hq=32, Hkv=8, d=128), each
+                 attending only within itself: TFLOP/s of the permitted pairs
+                 against 2.5 PFLOP/s.
   ring_decode    decode over a rolling cache of capacity w = 4096 with the new
                  cell committed in the call (B=32, Hq=8, Hkv=2, d=64, ragged
                  lengths in [1, 32768]): GB/s of the K/V cells in each row's
@@ -42,7 +46,7 @@ Prints ONE JSON line.
                  window 4096, linear cache: GB/s of the cells in the windows.
   small_f32_prefill  the fp32 prefill B=1, T=16, Hq=4, Hkv=2, d=8: us per
                  call (latency only), without a window and with window 2.
-  The prefix, rolling-cache, sweep and ragged legs time back-to-back calls
+  The prefix, packed, rolling-cache, sweep and ragged legs time back-to-back calls
   between two events, like `value`; `per_call_ms` adds events around each
   call, which for calls shorter than the binding's host time per call
   measures the host.
@@ -58,8 +62,8 @@ Prints ONE JSON line.
                  kernel source still has the hash they were taken with.
 
     python bench.py --leg NAME [--steps K] [--copy-calibration]
-runs one leg only (decode, prefill, prefix, ring, sweep8, sweep2, sweep1,
-ragged), for hardware-counter runs; and
+runs one leg only (decode, prefill, prefix, packed, ring, sweep8, sweep2,
+sweep1, ragged), for hardware-counter runs; and
     python bench.py --summarize-counters DIR
 turns the counter CSVs of those runs (DIR/<leg>/{fetch,write}/...) into the
 traffic summary committed under profiles/.
@@ -128,9 +132,10 @@ def measured_mfma():
 # kernels of one call (the first is launched once per call).
 LEG_SOURCE = {"decode": DECODE_SRC, "ring": DECODE_SRC, "sweep8": DECODE_SRC,
               "sweep2": DECODE_SRC, "sweep1": DECODE_SRC, "ragged": DECODE_SRC,
-              "prefill": PREFILL_SRC, "prefix": PREFILL_SRC}
+              "prefill": PREFILL_SRC, "prefix": PREFILL_SRC, "packed": PREFILL_SRC}
 LEG_KERNELS = {leg: ("decode_kernel", "decode_merge_kernel") for leg in LEG_SOURCE}
-LEG_KERNELS["prefill"] = LEG_KERNELS["prefix"] = ("prefill_mfma_kernel", "prefix_merge_kernel")
+LEG_KERNELS["prefill"] = LEG_KERNELS["prefix"] = LEG_KERNELS["packed"] = \
+    ("prefill_mfma_kernel", "prefix_merge_kernel")
 
 
 def _summary_values(path):
@@ -193,7 +198,8 @@ def _leg_counter_bytes(rows, leg):
 
 def algorithmic_bytes(leg):
     """The bytes each leg's workload must move, as the bench legs count them
-    (None for the prefill legs, whose roofline is matrix-core work)."""
+    (None for the causal and prefix prefill legs, whose roofline is
+    matrix-core work)."""
     from gqa_kv_cache_02_amd import synth
 
     if leg == "decode":
@@ -212,6 +218,9 @@ def algorithmic_bytes(leg):
         if leg == "ring":  # the candidate read and committed
             nbytes += 4 * c["B"] * c["Hkv"] * c["d"] * 2
         return nbytes
+    if leg == "packed":  # Q and K/V read once, O written once (its roofline is HBM)
+        c = synth.CONFIGS["packed_b1_t4096_hq32_hkv8_d128"]
+        return 2 * c["B"] * c["T"] * c["d"] * (2 * c["Hq"] + 2 * c["Hkv"])
     return None
 
 
@@ -229,7 +238,7 @@ def summarize_counters(dirpath):
         "# counters are scaled by what they read for it (factor = 1 GiB / counter).",
         "#",
         "# Commands (from the repository root; TMPDIR=/tmp), for every leg in",
-        "# decode prefill prefix ring sweep8 sweep2 sweep1 ragged:",
+        "# decode prefill prefix packed ring sweep8 sweep2 sweep1 ragged:",
         f"#   {cmd_f}",
         "#   (the same with --pmc WRITE_SIZE and -d OUT/<leg>/write)",
         "#   python3 bench.py --summarize-counters OUT",
@@ -259,7 +268,8 @@ def summarize_counters(dirpath):
         vals.append(f"{leg}.hbm_bytes_per_call = {int(round(rd + wt))}")
     lines.append("#")
     lines.append("# The prefill legs read Q and K/V and write O (and, for the split prefix")
-    lines.append("# rows, partials that the merge reads back); their roofline is matrix-core work.")
+    lines.append("# rows, partials that the merge reads back).  The causal and prefix legs'")
+    lines.append("# roofline is matrix-core work; the packed leg's short segments make it HBM.")
     lines += vals
     lines.append(f"decode_source_sha256_16 = {source_hash(DECODE_SRC)}")
     lines.append(f"prefill_source_sha256_16 = {source_hash(PREFILL_SRC)}")
@@ -453,6 +463,56 @@ def bench_prefix(torch, gqa, synth, steps, warmup, cpu=False):
         res["cpu_baseline"] = _oracle_baseline(
             lambda: oracle.attend_prefix(qn, kn, vn), flops, 1e12, "TFLOP/s",
             "the whole prefix workload (512 new rows against 4096 cells) in fp64")
+    return res
+
+
+def packed_pairs(seg_starts):
+    """Permitted pairs of one packed row: a cell at offset i of its segment
+    reads the i + 1 cells from the segment start (causal within it)."""
+    T = len(seg_starts)
+    starts = sorted(set(int(x) for x in seg_starts))
+    lens = [b - a for a, b in zip(starts, starts[1:] + [T])]
+    return sum(n * (n + 1) // 2 for n in lens), lens
+
+
+def bench_packed(torch, gqa, synth, steps, warmup, cpu=False):
+    cfg = synth.CONFIGS["packed_b1_t4096_hq32_hkv8_d128"]
+    B, T, hq, hkv, d = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    lo, hi = cfg["seg_len"]
+    dev = torch.device("cuda:0")
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, cfg["seed"], dev)
+    segs_cpu = synth.packed_segment_starts(B, T, lo, hi, cfg["seed"])
+    segs = segs_cpu.to(dev)
+    out = torch.empty((B, T, hq, d), dtype=torch.bfloat16, device=dev)
+    # a full row of new cells (qlens = seqlens = T): the key range is never
+    # split, so no workspace
+    assert gqa.prefill_prefix_workspace_bytes(B, T, T, hq, hkv, d) == 0
+    ms, ms_call = _time_calls(torch, lambda i: gqa.prefill_prefix(q, k, v, seg_starts=segs,
+                                                                  out=out), steps, warmup)
+    pairs, lens = packed_pairs(segs_cpu[0].tolist())
+    flops = 4 * hq * d * B * pairs
+    tflops = flops / (ms * 1e-3) / 1e12
+    # Q and K/V read once, O written once: with segments this short the
+    # workload moves more bytes per flop than the chip's balance point, so
+    # its roofline is the larger of the HBM and matrix-core times
+    nbytes = algorithmic_bytes("packed")
+    t_hbm, t_mfma = nbytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12)
+    res = dict(workload="gqa_prefill_packed_b1_t4096_hq32_hkv8_d128_bf16",
+               segments=lens, ms=round(ms, 5), flops=flops, tflops=round(tflops, 2),
+               frac_of_bf16_peak=round(tflops / BF16_PEAK_TFLOPS, 4),
+               bytes=nbytes, roofline_bound="hbm" if t_hbm >= t_mfma else "mfma",
+               roofline_us=round(max(t_hbm, t_mfma) * 1e6, 2),
+               frac_of_roofline=round(max(t_hbm, t_mfma) / (ms * 1e-3), 4),
+               tokens_per_s=round(B * T / (ms * 1e-3), 1), per_call_ms=round(ms_call, 5),
+               timing=f"{B2B}; {PER_CALL}", traffic=measured_traffic("packed"))
+    if cpu:
+        import oracle
+
+        qn, kn, vn = _f64(q), _f64(k), _f64(v)
+        sn = segs_cpu.numpy()
+        res["cpu_baseline"] = _oracle_baseline(
+            lambda: oracle.attend_prefix(qn, kn, vn, segs=sn), flops, 1e12, "TFLOP/s",
+            f"the whole packed workload ({len(lens)} sequences in one 4096-cell row) in fp64")
     return res
 
 
@@ -710,6 +770,8 @@ def run_leg(torch, gqa, synth, leg, steps, warmup):
         res = bench_prefill(torch, gqa, synth, steps, warmup)
     elif leg == "prefix":
         res = bench_prefix(torch, gqa, synth, steps, warmup)
+    elif leg == "packed":
+        res = bench_packed(torch, gqa, synth, steps, warmup)
     elif leg == "ring":
         res = bench_ring(torch, gqa, synth, steps, warmup)
     elif leg.startswith("sweep"):
@@ -793,6 +855,8 @@ def main():
     if not args.no_prefill:
         line["prefill"] = bench_prefill(torch, gqa, synth, max(10, args.steps // 10), 3, cpu)
         line["prefix_prefill"] = bench_prefix(torch, gqa, synth, max(10, args.steps // 10), 3,
+                                              cpu)
+        line["packed_prefill"] = bench_packed(torch, gqa, synth, max(10, args.steps // 10), 3,
                                               cpu)
     line["ring_decode"] = bench_ring(torch, gqa, synth, max(20, args.steps // 2), 10, cpu)
     line["decode_sweep"] = bench_sweep(torch, gqa, synth, max(20, args.steps // 2), 10, cpu)

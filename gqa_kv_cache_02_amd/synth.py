@@ -12,7 +12,7 @@ Workloads (no public dataset is involved; shapes follow the pages' examples):
   (j+1, 0) on KV head 0 and (0, 10(j+1)) on KV head 1 (embedding feature 0 of
   cell j is j+1 and the value projection maps it to features 0 and 3, as the
   worked_example code in that section builds them).
-* ``CONFIGS`` -- the five measured or checked workloads, Q/K/V iid N(0,1)
+* ``CONFIGS`` -- the measured or checked workloads, Q/K/V iid N(0,1)
   drawn in float32 from a seeded generator and rounded to bf16 (round to
   nearest even) where the dtype is bf16.
 """
@@ -50,6 +50,12 @@ CONFIGS = {
     # committed in the same call.
     "ring_b32_hq8_hkv2_d64_w4096": dict(kind="ring", dtype="bf16", B=32, Hq=8, Hkv=2, d=64,
                                         n=(1, 32768), window=4096, seed=1007),
+    # Packed segments: independent sequences of 64..1024 cells (uniform,
+    # seeded; the last one cut to fill the row) back to back in one causal
+    # prefill row of 4096 cells, each attending only within itself.
+    "packed_b1_t4096_hq32_hkv8_d128": dict(kind="packed", dtype="bf16", B=1, T=4096, Hq=32,
+                                           Hkv=8, d=128, seg_len=(64, 1024), window=None,
+                                           seed=1008),
 }
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
@@ -93,6 +99,20 @@ def ragged_lengths(B: int, lo: int, hi: int, seed: int) -> torch.Tensor:
     """Per-sequence lengths uniform in [lo, hi] (inclusive), int32, on the CPU."""
     g = _gen(seed, "cpu")
     return torch.randint(lo, hi + 1, (B,), generator=g, dtype=torch.int64).to(torch.int32)
+
+
+def packed_segment_starts(B: int, T: int, lo: int, hi: int, seed: int) -> torch.Tensor:
+    """Segment starts [B, T] int32 (CPU) of sequences packed back to back:
+    lengths uniform in [lo, hi], the last one of each row cut at T."""
+    g = _gen(seed, "cpu")
+    starts = torch.empty((B, T), dtype=torch.int32)
+    for b in range(B):
+        t = 0
+        while t < T:
+            n = int(torch.randint(lo, hi + 1, (1,), generator=g))
+            starts[b, t:t + n] = t
+            t += n
+    return starts
 
 
 def fixture_4token(dtype=torch.float32, device="cpu"):

@@ -105,6 +105,20 @@ def test_traffic_summary_per_leg(tmp_path):
     assert vals["prefill_source_sha256_16"] == bench.source_hash(bench.PREFILL_SRC)
 
 
+def test_packed_pairs():
+    # segments of 3 and 2 cells: 1 + 2 + 3 and 1 + 2 permitted pairs
+    assert bench.packed_pairs([0, 0, 0, 3, 3]) == (9, [3, 2])
+    assert bench.packed_pairs([0] * 7) == (28, [7])
+    from gqa_kv_cache_02_amd import synth
+    c = synth.CONFIGS["packed_b1_t4096_hq32_hkv8_d128"]
+    segs = synth.packed_segment_starts(1, c["T"], *c["seg_len"], c["seed"])[0].tolist()
+    pairs, lens = bench.packed_pairs(segs)
+    assert sum(lens) == c["T"] and all(64 <= n <= 1024 for n in lens[:-1])
+    assert pairs == sum(n * (n + 1) // 2 for n in lens)
+    # Q and O of 32 heads, K and V of 8, 4096 cells of 128 bf16 features
+    assert bench.algorithmic_bytes("packed") == 2 * 4096 * 128 * (2 * 32 + 2 * 8) == 83_886_080
+
+
 def test_algorithmic_bytes_of_the_legs():
     assert bench.algorithmic_bytes("decode") == 262_275_072
     assert bench.algorithmic_bytes("sweep1") == 65_601_536

@@ -287,6 +287,36 @@ def test_full_chunked_prefill_t512_c4096():
     assert (r[..., 4] == xor_to).all()
 
 
+def test_full_packed_prefill_t4096():
+    cfg = synth.CONFIGS["packed_b1_t4096_hq32_hkv8_d128"]
+    B, T, hq, hkv, d = cfg["B"], cfg["T"], cfg["Hq"], cfg["Hkv"], cfg["d"]
+    lo, hi = cfg["seg_len"]
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, cfg["seed"], DEV)
+    segs = synth.packed_segment_starts(B, T, lo, hi, cfg["seed"]).numpy()
+    out, rec = run_prefix(q, k, v, None, None, segs, None)
+    # the instantiation bench.py times (no records), called as it calls it
+    plain = torch.empty_like(out)
+    gqa.prefill_prefix(q, k, v, seg_starts=torch.from_numpy(segs).to(DEV), out=plain)
+    torch.cuda.synchronize()
+    assert torch.equal(plain, out)
+    # every output element and every row's record against the oracle
+    ref, _, rrec = oracle.attend_prefix(_np(q), _np(k), _np(v), segs=segs, want_records=True)
+    err = _maxerr(_np(out), ref)
+    assert err <= BF16_TOL, err
+    r = _np(rec).astype(np.int32)
+    assert np.array_equal(r, rrec)
+    # closed form: cell t reads keys s..t of its own segment (start s), so the
+    # count is t - s + 1 and the XOR is that of s..t
+    t = np.arange(T)[None, :, None]
+    s0 = segs[:, :, None].astype(np.int64)
+
+    def xor_upto(n):  # XOR of 0..n (n >= -1)
+        return np.where(n % 4 == 0, n, np.where(n % 4 == 1, 1, np.where(n % 4 == 2, n + 1, 0)))
+
+    assert (r[..., 1] == s0).all() and (r[..., 2] == t).all() and (r[..., 3] == t - s0 + 1).all()
+    assert (r[..., 4] == (xor_upto(t) ^ xor_upto(s0 - 1))).all()
+
+
 def test_full_ring_decode_ragged_w4096():
     cfg = synth.CONFIGS["ring_b32_hq8_hkv2_d64_w4096"]
     B, hq, hkv, d, w = cfg["B"], cfg["Hq"], cfg["Hkv"], cfg["d"], cfg["window"]
