@@ -153,7 +153,7 @@ int prefill_impl(const void *q, const void *k, const void *v, void *out, const i
         plan.nsplit = 1;
         if (x.prefix)
             plan = gqa::plan_prefix(B, T, C, Hq, Hkv, d, window);
-        if (!gqa::prefill_grid_ok(B, T, Hq, Hkv, plan.nsplit))
+        if (!gqa::prefill_grid_ok(B, T, Hq, Hkv, plan.nsplit, gqa::prefill_waves(x.segs != nullptr)))
             return GQA_ERR_SHAPE;
         if (plan.nsplit > 1) {
             if (!x.workspace)

@@ -87,6 +87,7 @@ PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window);
 
 hipError_t launch_prefill_mfma(const Problem &p, const PrefixPlan &plan, void *workspace,
                                hipStream_t stream);
-bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit);
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit, int nw);
+int prefill_waves(bool segmented);
 
 } // namespace gqa

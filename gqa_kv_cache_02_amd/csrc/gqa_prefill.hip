@@ -36,7 +36,8 @@ namespace gqa {
 
 constexpr int kPBN = 64;   // keys per K/V tile
 constexpr int kPRows = 32; // query rows per wavefront
-constexpr int kPWaves = 8; // wavefronts per workgroup
+constexpr int kPWaves = 8; // wavefronts per workgroup (4 for packed segments, see
+                           // prefill_waves)
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
 
@@ -276,15 +277,18 @@ template <int D, bool kRecord> struct TileMath {
     }
 };
 
-template <int D, bool kRecord>
-__global__ __launch_bounds__(kPWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// NW wavefronts per workgroup: 8 (one workgroup per CU, two wavefronts per
+// SIMD) or 4 (two workgroups per CU, so that one's row loads and output
+// writes overlap the other's tiles; used where blocks carry little work).
+template <int D, bool kRecord, int NW>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_mfma_kernel(PrefillArgs a) {
     using L = PrefillLayout<D>;
     using TM = TileMath<D, kRecord>;
     constexpr int KS = D / 16;   // 16-feature k-steps of Q.K (32x32x16)
     constexpr int DB = D / 32;   // 32-column blocks of P.V
     constexpr int CPR = L::CPR;
-    constexpr int NLD = CPR / kPWaves; // 1 KiB direct loads per wavefront per tensor per tile
+    constexpr int NLD = CPR / NW; // 1 KiB direct loads per wavefront per tensor per tile
 
     // Two stages of [K | V] tiles.  Separate objects (and a loop unrolled by
     // two) let the compiler see that reads of one stage never alias the
@@ -350,7 +354,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const int w_lo_last = wave_max_i(row_on ? lo_row : -1);
     const int w_last = wave_max_i(row_on ? my_pos : -1);        // -1: no active row
     const int w_first = wave_min_i(row_on ? my_pos : INT_MAX);
-    __shared__ int sm_range[kPWaves][2];
+    __shared__ int sm_range[NW][2];
     if (lane == 0) {
         sm_range[wave][0] = w_lo;
         sm_range[wave][1] = w_last;
@@ -358,7 +362,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     __syncthreads();
     int wg_lo = INT_MAX, wg_last = -1;
 #pragma unroll
-    for (int w = 0; w < kPWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
         wg_lo = min(wg_lo, sm_range[w][0]);
         wg_last = max(wg_last, sm_range[w][1]);
     }
@@ -451,7 +455,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     const uint16_t *vbase = a.v + kv_off;
 
     // Direct loads of one tile into a stage: wavefront w issues loads
-    // ii = it*8 + w; lane l fills linear chunk ii*64 + l, i.e. row
+    // ii = it*NW + w; lane l fills linear chunk ii*64 + l, i.e. row
     // (ii*64 + l) / CPR and slot (ii*64 + l) % CPR, with the global chunk the
     // swizzle puts there.  An interior tile uses per-lane byte offsets fixed
     // for the whole loop; the workgroup's last tile repeats its last key in
@@ -459,7 +463,7 @@ void prefill_mfma_kernel(PrefillArgs a) {
     uint32_t koffs[NLD], voffs[NLD];
 #pragma unroll
     for (int it = 0; it < NLD; ++it) {
-        const int ii = it * kPWaves + wave_u;
+        const int ii = it * NW + wave_u;
         const int lin = ii * 64 + lane;
         const int row = lin / CPR;
         const int slot = lin % CPR;
@@ -473,14 +477,14 @@ void prefill_mfma_kernel(PrefillArgs a) {
             const void *vb0 = vbase + (int64_t)j0 * D;
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
-                const int ii = it * kPWaves + wave_u;
+                const int ii = it * NW + wave_u;
                 dma16s(kb0, koffs[it], dst + ii * 1024);
                 dma16s(vb0, voffs[it], dst + L::kTileBytes + ii * 1024);
             }
         } else {
 #pragma unroll
             for (int it = 0; it < NLD; ++it) {
-                const int ii = it * kPWaves + wave_u;
+                const int ii = it * NW + wave_u;
                 const int lin = ii * 64 + lane;
                 const int row = lin / CPR;
                 const int slot = lin % CPR;
@@ -708,31 +712,39 @@ __global__ __launch_bounds__(256) void prefix_merge_kernel(PrefillArgs a) {
     }
 }
 
-// Heads per workgroup: the largest power of two (at most 8) that divides r;
+// Wavefronts per workgroup.  Packed segments leave each block of rows only
+// the tiles of its own segment, often a few, against a fixed cost per
+// workgroup (its rows' queries loaded, its output written); two 4-wavefront
+// workgroups per CU overlap that cost with the other's tiles (57.3 -> 50.9
+// us on 4096 cells of 7 packed sequences, against 138.7 -> 149.4 us for a
+// plain causal prefill, whose blocks are heavy).
+int prefill_waves(bool segmented) { return segmented ? 4 : kPWaves; }
+
+// Heads per workgroup: the largest power of two (at most nw) that divides r;
 // the remaining wavefronts take further 32-row blocks of the same heads, so
-// every workgroup runs all 8 wavefronts.  (One staged tile feeds 8
-// wavefronts whatever the split between heads and rows; more heads mean
+// every workgroup runs all nw wavefronts.  (One staged tile feeds every
+// wavefront whatever the split between heads and rows; more heads mean
 // fewer rows per workgroup and less work on the causal diagonal.)
-static void prefill_shape(int r, int *hpw, int *rb) {
-    int x = kPWaves;
+static void prefill_shape(int r, int nw, int *hpw, int *rb) {
+    int x = nw;
     while (r % x != 0)
         x /= 2;
     *hpw = x;
-    *rb = kPWaves / x;
+    *rb = nw / x;
 }
 
 // The grid is one-dimensional: ceil(T / (32*rb)) * B * Hkv * (r/hpw)
-// workgroups of 512 work-items, whose total must fit a 32-bit count.
-static int64_t prefill_workgroups(int B, int T, int Hq, int Hkv) {
+// workgroups of nw*64 work-items, whose total must fit a 32-bit count.
+static int64_t prefill_workgroups(int B, int T, int Hq, int Hkv, int nw) {
     int hpw, rb;
-    prefill_shape(Hq / Hkv, &hpw, &rb);
+    prefill_shape(Hq / Hkv, nw, &hpw, &rb);
     const int64_t nqb = ((int64_t)T + kPRows * rb - 1) / (kPRows * rb);
     return nqb * B * Hkv * ((Hq / Hkv) / hpw);
 }
 
-bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit) {
-    const int64_t wgs = prefill_workgroups(B, T, Hq, Hkv) * (nsplit > 1 ? nsplit : 1);
-    return T >= 0 && wgs * kPWaves * 64 <= (int64_t)UINT32_MAX &&
+bool prefill_grid_ok(int B, int T, int Hq, int Hkv, int nsplit, int nw) {
+    const int64_t wgs = prefill_workgroups(B, T, Hq, Hkv, nw) * (nsplit > 1 ? nsplit : 1);
+    return T >= 0 && wgs * nw * 64 <= (int64_t)UINT32_MAX &&
            (int64_t)B * T * Hq * 64 <= (int64_t)UINT32_MAX; // merge grid
 }
 
@@ -747,8 +759,10 @@ PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window) 
     PrefixPlan p{};
     p.nsplit = 1;
     p.tps = 0;
+    // (counted for 8-wavefront workgroups whatever the call runs, so that the
+    // workspace size depends on the shape arguments only)
     int hpw, rb;
-    prefill_shape(Hq / Hkv, &hpw, &rb);
+    prefill_shape(Hq / Hkv, kPWaves, &hpw, &rb);
     const int64_t nqb = ((int64_t)T + kPRows * rb - 1) / (kPRows * rb);
     const int64_t units = nqb * B * Hkv * ((Hq / Hkv) / hpw);
     const int64_t elig = (window > 0 && window < C) ? window : C;
@@ -774,9 +788,9 @@ PrefixPlan plan_prefix(int B, int T, int C, int Hq, int Hkv, int d, int window) 
     return p;
 }
 
-template <int D, bool kRecord>
+template <int D, bool kRecord, int NW>
 static hipError_t launch_p(const PrefillArgs &a, dim3 grid, hipStream_t s) {
-    prefill_mfma_kernel<D, kRecord><<<grid, kPWaves * 64, 0, s>>>(a);
+    prefill_mfma_kernel<D, kRecord, NW><<<grid, NW * 64, 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit <= 1)
         return e;
@@ -799,7 +813,8 @@ hipError_t launch_prefill_mfma(const Problem &p, const PrefixPlan &plan, void *w
     a.records = p.records;
     a.T = p.T; a.C = p.C; a.Hq = p.Hq; a.Hkv = p.Hkv; a.window = p.window;
     a.r = p.Hq / p.Hkv;
-    prefill_shape(a.r, &a.hpw, &a.rb);
+    const int nw = prefill_waves(p.segs != nullptr);
+    prefill_shape(a.r, nw, &a.hpw, &a.rb);
     a.nhc = a.r / a.hpw;
     a.nqb = (p.T + kPRows * a.rb - 1) / (kPRows * a.rb);
     a.scale_log2 = fabsf(p.scale) * kLog2e;
@@ -811,11 +826,16 @@ hipError_t launch_prefill_mfma(const Problem &p, const PrefixPlan &plan, void *w
     a.o_part = a.nsplit > 1 ? reinterpret_cast<float *>(w + plan.o_off) : nullptr;
     a.lse_part = a.nsplit > 1 ? reinterpret_cast<float *>(w + plan.lse_off) : nullptr;
     a.rec_part = a.nsplit > 1 ? reinterpret_cast<int32_t *>(w + plan.rec_off) : nullptr;
-    dim3 grid(static_cast<uint32_t>(prefill_workgroups(p.B, p.T, p.Hq, p.Hkv) * a.nsplit), 1, 1);
+    dim3 grid(static_cast<uint32_t>(prefill_workgroups(p.B, p.T, p.Hq, p.Hkv, nw) * a.nsplit), 1, 1);
     const bool rec = p.records != nullptr;
+    if (nw == 4) {
+        if (p.d == 128)
+            return rec ? launch_p<128, true, 4>(a, grid, stream) : launch_p<128, false, 4>(a, grid, stream);
+        return rec ? launch_p<64, true, 4>(a, grid, stream) : launch_p<64, false, 4>(a, grid, stream);
+    }
     if (p.d == 128)
-        return rec ? launch_p<128, true>(a, grid, stream) : launch_p<128, false>(a, grid, stream);
-    return rec ? launch_p<64, true>(a, grid, stream) : launch_p<64, false>(a, grid, stream);
+        return rec ? launch_p<128, true, 8>(a, grid, stream) : launch_p<128, false, 8>(a, grid, stream);
+    return rec ? launch_p<64, true, 8>(a, grid, stream) : launch_p<64, false, 8>(a, grid, stream);
 }
 
 } // namespace gqa
