@@ -331,6 +331,20 @@ def test_binding_refuses_host_tensors():
         gqa.decode_cache(q[:, :, 0].contiguous(), k, k.clone())
 
 
+def test_missing_library_raises(monkeypatch):
+    """Without the built library every entry point raises: there is no
+    fallback path to run instead."""
+    import torch
+    monkeypatch.setattr(gqa, "_lib", None)
+    monkeypatch.setattr(gqa, "LIB_PATH", "/nonexistent/libgqa.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        gqa.lib()
+    q = torch.zeros((1, 4, 4, 8), dtype=torch.float32)
+    k = torch.zeros((1, 2, 4, 8), dtype=torch.float32)
+    with pytest.raises((RuntimeError, ValueError)):
+        gqa.prefill(q, k, k.clone())
+
+
 def _native_check():
     import __graft_entry__ as entry
     if not os.path.exists(entry.NATIVE_BIN):
