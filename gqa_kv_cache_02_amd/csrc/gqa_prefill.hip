@@ -5,13 +5,14 @@
 // matrix; the dense pairwise work remains).
 //
 // Work decomposition.  A workgroup owns one batch row b, one KV group g and
-// one block of query rows, and runs 8 wavefronts (one workgroup per CU, two
-// wavefronts per SIMD): `hpw` query heads of group g times `rb` blocks of 32
-// rows (hpw * rb = 8).  All its wavefronts read the same K/V tiles, which are
+// one block of query rows, and runs NW wavefronts: 8 (one workgroup per CU,
+// two wavefronts per SIMD), or 4 for packed segments (two workgroups per CU).
+// They are `hpw` query heads of group g times `rb` blocks of 32 rows
+// (hpw * rb = NW).  All its wavefronts read the same K/V tiles, which are
 // staged once in LDS per workgroup -- the r query heads that share a KV head
 // ("Share key/value heads and make context explicit", "Give each query head
 // an explicit shared KV head") never cause a second read or a repeated copy,
-// and one staged tile feeds 8 wavefronts.
+// and one staged tile feeds every wavefront of the workgroup.
 //
 // Per 64-key tile and wavefront (32 query rows):
 //   S^T[64 keys x 32 rows] = K[64 x d] . Q^T[d x 32]     (MFMA 32x32x16 bf16)
