@@ -160,6 +160,36 @@ def test_segments_sweep(dtype, d):
         check_prefix(q, k, v, n, n, segs, w, "arbitrary")
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_many_head_chunks(d):
+    """64 query heads on one KV head: the decode splits them into 4 chunks of
+    16, the prefill into 8 chunks of 8 heads, and packed segments (4-wavefront
+    workgroups) into 16 chunks of 4; every chunk must land on its own heads."""
+    hq, hkv = 64, 1
+    B, C = 2, 300
+    q, k, v = synth.decode_inputs(B, C, hq, hkv, d, torch.bfloat16, 3800 + d, DEV)
+    n = [300, 77]
+    for w in (None, 65):
+        rec = torch.full((B, hq, 5), -7, dtype=torch.int32, device=DEV)
+        out = gqa.decode(q, k, v, seqlens=_i32(n), window=w, records=rec)
+        torch.cuda.synchronize()
+        ref, _, rrec = oracle.decode(_np(q), _np(k), _np(v), seqlens=n, window=w, want_records=True)
+        assert _maxerr(_np(out), ref) <= BF16_TOL, ("decode", w)
+        assert np.array_equal(_np(rec).astype(np.int32), rrec), ("decode", w)
+    T = 150
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, 3810 + d, DEV)
+    n = [150, 61]
+    for w in (None, 65):
+        rec = torch.full((B, T, hq, 5), -7, dtype=torch.int32, device=DEV)
+        out = gqa.prefill(q, k, v, seqlens=_i32(n), window=w, records=rec)
+        torch.cuda.synchronize()
+        ref, _, rrec = oracle.prefill(_np(q), _np(k), _np(v), seqlens=n, window=w, want_records=True)
+        assert _maxerr(_np(out), ref) <= BF16_TOL, ("prefill", w)
+        assert np.array_equal(_np(rec).astype(np.int32), rrec), ("prefill", w)
+    segs = _packed_segments(B, T, 3820 + d, 40)
+    check_prefix(q, k, v, n, n, segs, None, ("packed", hq, hkv))
+
+
 def test_packing_equals_separate_runs():
     hq, hkv, d = 8, 2, 128
     la, lb = 137, 200
