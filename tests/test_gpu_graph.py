@@ -135,3 +135,63 @@ def test_prefix_and_rolling_decode_replay_in_a_graph():
         if i == 1:
             o, _, _ = oracle.attend_prefix(_np(q), _np(k), _np(v), seqlens=[1900], qlens=[64])
             assert float(np.max(np.abs(_np(outp) - o))) <= 2e-2
+
+
+def test_packed_segments_replay_in_a_graph():
+    # packed segments run the 4-wavefront workgroups: once over a whole packed
+    # row, once as new rows against a long cache (key range split, merge)
+    B, T, hq, hkv, d = 2, 300, 8, 2, 128
+    q, k, v = synth.prefill_inputs(B, T, hq, hkv, d, torch.bfloat16, 5700, DEV)
+    segs_np = np.zeros((B, T), np.int32)
+    for b, cuts in enumerate(([0, 37, 120, 121, 250], [0, 64, 65, 200])):
+        for i, c in enumerate(cuts):
+            end = cuts[i + 1] if i + 1 < len(cuts) else T
+            segs_np[b, c:end] = c
+    segs = torch.from_numpy(segs_np).to(DEV)
+    out = torch.empty((B, T, hq, d), dtype=torch.bfloat16, device=DEV)
+
+    Tq, C = 64, 2000
+    qs, ks, vs = synth.prefill_inputs(1, Tq, hq, hkv, d, torch.bfloat16, 5701, DEV, C=C)
+    s_lens = torch.tensor([1900], dtype=torch.int32, device=DEV)
+    q_lens = torch.tensor([64], dtype=torch.int32, device=DEV)
+    segs_s_np = np.full((1, Tq), 1850, np.int32)
+    segs_s_np[0, 40:] = 1876
+    segs_s = torch.from_numpy(segs_s_np).to(DEV)
+    need = gqa.prefill_prefix_workspace_bytes(1, Tq, C, hq, hkv, d)
+    assert need > 0  # the split path
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    outs = torch.empty((1, Tq, hq, d), dtype=torch.bfloat16, device=DEV)
+
+    def calls():
+        gqa.prefill_prefix(q, k, v, seg_starts=segs, out=out)
+        gqa.prefill_prefix(qs, ks, vs, seqlens=s_lens, qlens=q_lens, seg_starts=segs_s, out=outs,
+                           workspace=ws)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    torch.cuda.synchronize()
+
+    for i in range(4):
+        q.copy_(synth.randn((B, hq, T, d), 5800 + i, torch.bfloat16, DEV))
+        qs.copy_(synth.randn((1, hq, Tq, d), 5900 + i, torch.bfloat16, DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        ref = gqa.prefill_prefix(q, k, v, seg_starts=segs)
+        refs = gqa.prefill_prefix(qs, ks, vs, seqlens=s_lens, qlens=q_lens, seg_starts=segs_s)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"packed replay {i} differs from the eager call"
+        assert torch.equal(outs, refs), f"split packed replay {i} differs from the eager call"
+        if i == 2:
+            o, _, _ = oracle.attend_prefix(_np(q), _np(k), _np(v), segs=segs_np)
+            assert float(np.max(np.abs(_np(out) - o))) <= 2e-2
+            o, _, _ = oracle.attend_prefix(_np(qs), _np(ks), _np(vs), seqlens=[1900], qlens=[64],
+                                           segs=segs_s_np)
+            assert float(np.max(np.abs(_np(outs) - o))) <= 2e-2
